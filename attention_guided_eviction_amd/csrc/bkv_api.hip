@@ -1,0 +1,336 @@
+// Host side of the libbkv C ABI (include/bkv.h): argument checks, workspace sizing,
+// splitting long models into launches of at most kMaxLayers layers, and launches.
+// Nothing here allocates, frees or synchronises.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "bkv_internal.h"
+
+namespace bkv {
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Multiply sizes, returning false on overflow.
+bool mul_ok(size_t a, size_t b, size_t* out) {
+  if (a != 0 && b > SIZE_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+bkv_status check_shape(const bkv_shape* s) {
+  if (s == nullptr || s->seq_len == nullptr) return BKV_EINVAL;
+  if (s->n_layers < 1 || s->batch < 1 || s->n_q_heads < 1 || s->n_kv_heads < 1 || s->capacity < 1 ||
+      s->head_dim < 1)
+    return BKV_EINVAL;
+  if (s->n_q_heads % s->n_kv_heads != 0) return BKV_EINVAL;
+  if (s->head_dim != 64 && s->head_dim != 128) return BKV_EUNSUPPORTED;
+  return BKV_OK;
+}
+
+template <typename T>
+bool all_set(T const* arr, int n) {
+  if (arr == nullptr) return false;
+  for (int i = 0; i < n; ++i)
+    if (arr[i] == nullptr) return false;
+  return true;
+}
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return na > 0 && nb > 0 && x < y + nb && y < x + na;
+}
+
+// Bytes of one layer of a [batch][heads][rows][cols] array of `elem`-byte items.
+size_t layer_bytes(const bkv_shape* s, int heads, long long rows, long long cols, size_t elem) {
+  size_t n = 1;
+  if (!mul_ok(n, static_cast<size_t>(s->batch), &n) || !mul_ok(n, static_cast<size_t>(heads), &n) ||
+      !mul_ok(n, static_cast<size_t>(rows), &n) || !mul_ok(n, static_cast<size_t>(cols), &n) ||
+      !mul_ok(n, elem, &n))
+    return SIZE_MAX;
+  return n;
+}
+
+int obs_pad_of(const bkv_shape* s, int window, int nb_max) {
+  const int g = s->n_q_heads / s->n_kv_heads;
+  return round_up(g * window + nb_max, 32);
+}
+
+int layers_per_launch(const bkv_shape* s) { return std::min(s->n_layers, kMaxLayers); }
+
+struct ScoreWs {
+  size_t part_bytes, lse_bytes, total;
+};
+
+ScoreWs score_ws(const bkv_shape* s, int window, int nb_max) {
+  ScoreWs w{};
+  const size_t units = static_cast<size_t>(layers_per_launch(s)) * s->batch * s->n_kv_heads;
+  const size_t tiles = (static_cast<size_t>(s->capacity) + kScoreTile - 1) / kScoreTile;
+  const size_t obs = static_cast<size_t>(obs_pad_of(s, window, nb_max));
+  w.part_bytes = align_up(units * tiles * obs * sizeof(float));
+  w.lse_bytes = align_up(units * obs * sizeof(float));
+  w.total = 2 * w.part_bytes + w.lse_bytes;
+  return w;
+}
+
+bkv_status check_score_args(const bkv_shape* s, const void* const* k, const void* const* q, int32_t q_len,
+                            int32_t window, const void* const* beacons, const int32_t* const* n_beacons,
+                            int32_t nb_max, float* const* scores) {
+  bkv_status st = check_shape(s);
+  if (st != BKV_OK) return st;
+  if (q_len < 0 || window < 0 || window > q_len || nb_max < 0) return BKV_EINVAL;
+  if (!all_set(k, s->n_layers) || !all_set(scores, s->n_layers)) return BKV_EINVAL;
+  if (window > 0 && !all_set(q, s->n_layers)) return BKV_EINVAL;
+  if (nb_max > 0 && (!all_set(beacons, s->n_layers) || !all_set(n_beacons, s->n_layers))) return BKV_EINVAL;
+  const int g = s->n_q_heads / s->n_kv_heads;
+  if (static_cast<long long>(g) * window + nb_max > BKV_MAX_OBS) return BKV_EUNSUPPORTED;
+  const size_t kb = layer_bytes(s, s->n_kv_heads, s->capacity, s->head_dim, 2);
+  const size_t sb = layer_bytes(s, s->n_kv_heads, s->capacity, 1, 4);
+  if (kb == SIZE_MAX || sb == SIZE_MAX) return BKV_EINVAL;
+  for (int l = 0; l < s->n_layers; ++l)
+    if (overlap(scores[l], sb, k[l], kb)) return BKV_EALIAS;
+  return BKV_OK;
+}
+
+bkv_status check_select_args(const bkv_shape* s, const float* const* scores, int32_t budget, int32_t window,
+                             int32_t* const* idx, int32_t* const* n_kept) {
+  bkv_status st = check_shape(s);
+  if (st != BKV_OK) return st;
+  if (budget < 1 || window < 0 || window > budget) return BKV_EINVAL;
+  if (!all_set(scores, s->n_layers) || !all_set(idx, s->n_layers) || !all_set(n_kept, s->n_layers))
+    return BKV_EINVAL;
+  if (s->capacity > 64 * kSelectThreads) return BKV_EUNSUPPORTED;
+  const size_t sb = layer_bytes(s, s->n_kv_heads, s->capacity, 1, 4);
+  const size_t ib = layer_bytes(s, s->n_kv_heads, budget, 1, 4);
+  const size_t nb = layer_bytes(s, s->n_kv_heads, 1, 1, 4);
+  if (sb == SIZE_MAX || ib == SIZE_MAX) return BKV_EINVAL;
+  for (int l = 0; l < s->n_layers; ++l)
+    if (overlap(idx[l], ib, scores[l], sb) || overlap(n_kept[l], nb, scores[l], sb) ||
+        overlap(n_kept[l], nb, idx[l], ib))
+      return BKV_EALIAS;
+  return BKV_OK;
+}
+
+bkv_status check_compact_args(const bkv_shape* s, const void* const* k, const void* const* v,
+                              const int32_t* const* idx, const int32_t* const* n_kept, int32_t budget,
+                              void* const* k_out, void* const* v_out) {
+  bkv_status st = check_shape(s);
+  if (st != BKV_OK) return st;
+  if (budget < 1) return BKV_EINVAL;
+  if (!all_set(k, s->n_layers) || !all_set(v, s->n_layers) || !all_set(idx, s->n_layers) ||
+      !all_set(n_kept, s->n_layers) || !all_set(k_out, s->n_layers) || !all_set(v_out, s->n_layers))
+    return BKV_EINVAL;
+  const size_t kb = layer_bytes(s, s->n_kv_heads, s->capacity, s->head_dim, 2);
+  const size_t ob = layer_bytes(s, s->n_kv_heads, budget, s->head_dim, 2);
+  if (kb == SIZE_MAX || ob == SIZE_MAX) return BKV_EINVAL;
+  for (int l = 0; l < s->n_layers; ++l) {
+    if (overlap(k_out[l], ob, k[l], kb) || overlap(k_out[l], ob, v[l], kb) || overlap(v_out[l], ob, k[l], kb) ||
+        overlap(v_out[l], ob, v[l], kb) || overlap(k_out[l], ob, v_out[l], ob))
+      return BKV_EALIAS;
+  }
+  return BKV_OK;
+}
+
+bkv_status hip_status(hipError_t e) { return e == hipSuccess ? BKV_OK : BKV_EHIP; }
+
+}  // namespace
+}  // namespace bkv
+
+using namespace bkv;
+
+extern "C" {
+
+const char* bkv_status_string(bkv_status status) {
+  switch (status) {
+    case BKV_OK: return "BKV_OK: success";
+    case BKV_EINVAL: return "BKV_EINVAL: invalid argument";
+    case BKV_EUNSUPPORTED: return "BKV_EUNSUPPORTED: valid but unsupported size or head_dim";
+    case BKV_EALIAS: return "BKV_EALIAS: output overlaps an input";
+    case BKV_EWORKSPACE: return "BKV_EWORKSPACE: workspace missing or too small";
+    case BKV_EHIP: return "BKV_EHIP: HIP runtime or launch failure";
+  }
+  return "BKV_?: unknown status";
+}
+
+const char* bkv_version(void) { return "0.1.0"; }
+
+size_t bkv_score_workspace_bytes(const bkv_shape* shape, int32_t window, int32_t nb_max) {
+  if (check_shape(shape) != BKV_OK || window < 0 || nb_max < 0) return 0;
+  return score_ws(shape, window, nb_max).total;
+}
+
+bkv_status bkv_score(const bkv_shape* shape, const void* const* k, const void* const* q, int32_t q_len,
+                     int32_t window, const void* const* beacons, const int32_t* const* n_beacons, int32_t nb_max,
+                     float* const* scores, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  bkv_status st = check_score_args(shape, k, q, q_len, window, beacons, n_beacons, nb_max, scores);
+  if (st != BKV_OK) return st;
+  const ScoreWs ws = score_ws(shape, window, nb_max);
+  if (workspace == nullptr || workspace_bytes < ws.total ||
+      reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
+    return BKV_EWORKSPACE;
+  ScoreArgs a;
+  memset(&a, 0, sizeof(a));
+  a.seq_len = shape->seq_len;
+  a.part_m = static_cast<float*>(workspace);
+  a.part_z = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.part_bytes);
+  a.lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * ws.part_bytes);
+  a.batch = shape->batch;
+  a.n_q_heads = shape->n_q_heads;
+  a.n_kv_heads = shape->n_kv_heads;
+  a.group = shape->n_q_heads / shape->n_kv_heads;
+  a.capacity = shape->capacity;
+  a.q_len = q_len;
+  a.window = window;
+  a.nb_max = nb_max;
+  a.obs_pad = obs_pad_of(shape, window, nb_max);
+  a.tiles = (shape->capacity + kScoreTile - 1) / kScoreTile;
+  a.scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(shape->head_dim)));
+  for (int l0 = 0; l0 < shape->n_layers; l0 += kMaxLayers) {
+    const int nl = std::min(kMaxLayers, shape->n_layers - l0);
+    for (int i = 0; i < nl; ++i) {
+      a.k[i] = static_cast<const uint16_t*>(k[l0 + i]);
+      a.q[i] = window > 0 ? static_cast<const uint16_t*>(q[l0 + i]) : nullptr;
+      a.beacons[i] = nb_max > 0 ? static_cast<const uint16_t*>(beacons[l0 + i]) : nullptr;
+      a.n_beacons[i] = nb_max > 0 ? n_beacons[l0 + i] : nullptr;
+      a.scores[i] = scores[l0 + i];
+    }
+    a.units = nl * shape->batch * shape->n_kv_heads;
+    st = hip_status(launch_score(a, nl, shape->head_dim, stream));
+    if (st != BKV_OK) return st;
+  }
+  return BKV_OK;
+}
+
+size_t bkv_select_workspace_bytes(const bkv_shape* shape, int32_t budget) {
+  (void)shape;
+  (void)budget;
+  return 0;
+}
+
+bkv_status bkv_select_topk(const bkv_shape* shape, const float* const* scores, int32_t budget, int32_t window,
+                           int32_t* const* idx, int32_t* const* n_kept, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  bkv_status st = check_select_args(shape, scores, budget, window, idx, n_kept);
+  if (st != BKV_OK) return st;
+  SelectArgs a;
+  memset(&a, 0, sizeof(a));
+  a.seq_len = shape->seq_len;
+  a.batch = shape->batch;
+  a.n_kv_heads = shape->n_kv_heads;
+  a.capacity = shape->capacity;
+  a.budget = budget;
+  a.window = window;
+  for (int l0 = 0; l0 < shape->n_layers; l0 += kMaxLayers) {
+    const int nl = std::min(kMaxLayers, shape->n_layers - l0);
+    for (int i = 0; i < nl; ++i) {
+      a.scores[i] = scores[l0 + i];
+      a.idx[i] = idx[l0 + i];
+      a.n_kept[i] = n_kept[l0 + i];
+    }
+    st = hip_status(launch_select(a, nl, stream));
+    if (st != BKV_OK) return st;
+  }
+  return BKV_OK;
+}
+
+bkv_status bkv_compact(const bkv_shape* shape, const void* const* k, const void* const* v,
+                       const int32_t* const* idx, const int32_t* const* n_kept, int32_t budget, void* const* k_out,
+                       void* const* v_out, hipStream_t stream) {
+  bkv_status st = check_compact_args(shape, k, v, idx, n_kept, budget, k_out, v_out);
+  if (st != BKV_OK) return st;
+  CompactArgs a;
+  memset(&a, 0, sizeof(a));
+  a.batch = shape->batch;
+  a.n_kv_heads = shape->n_kv_heads;
+  a.capacity = shape->capacity;
+  a.budget = budget;
+  for (int l0 = 0; l0 < shape->n_layers; l0 += kMaxLayers) {
+    const int nl = std::min(kMaxLayers, shape->n_layers - l0);
+    for (int i = 0; i < nl; ++i) {
+      a.k[i] = static_cast<const uint16_t*>(k[l0 + i]);
+      a.v[i] = static_cast<const uint16_t*>(v[l0 + i]);
+      a.idx[i] = idx[l0 + i];
+      a.n_kept[i] = n_kept[l0 + i];
+      a.k_out[i] = static_cast<uint16_t*>(k_out[l0 + i]);
+      a.v_out[i] = static_cast<uint16_t*>(v_out[l0 + i]);
+    }
+    st = hip_status(launch_compact(a, nl, shape->head_dim, stream));
+    if (st != BKV_OK) return st;
+  }
+  return BKV_OK;
+}
+
+bkv_status bkv_update_beacons(const bkv_shape* shape, const void* const* beacons_in, const int32_t* const* n_in,
+                              int32_t nb_max, const void* const* q_new, int32_t q_len, int32_t t_new,
+                              void* const* beacons_out, int32_t* const* n_out, hipStream_t stream) {
+  bkv_status st = check_shape(shape);
+  if (st != BKV_OK) return st;
+  if (nb_max < 1 || q_len < 0 || t_new < 0 || t_new > q_len) return BKV_EINVAL;
+  if (!all_set(beacons_in, shape->n_layers) || !all_set(n_in, shape->n_layers) ||
+      !all_set(beacons_out, shape->n_layers) || !all_set(n_out, shape->n_layers))
+    return BKV_EINVAL;
+  if (t_new > 0 && !all_set(q_new, shape->n_layers)) return BKV_EINVAL;
+  const int g = shape->n_q_heads / shape->n_kv_heads;
+  const long long pool_max = nb_max + static_cast<long long>(g) * t_new;
+  if (pool_max > BKV_MAX_POOL) return BKV_EUNSUPPORTED;
+  const size_t bb = layer_bytes(shape, shape->n_kv_heads, nb_max, shape->head_dim, 2);
+  const size_t qb = layer_bytes(shape, shape->n_q_heads, q_len, shape->head_dim, 2);
+  const size_t cb = layer_bytes(shape, shape->n_kv_heads, 1, 1, 4);
+  if (bb == SIZE_MAX || qb == SIZE_MAX) return BKV_EINVAL;
+  for (int l = 0; l < shape->n_layers; ++l) {
+    if (overlap(beacons_out[l], bb, beacons_in[l], bb) || overlap(n_out[l], cb, n_in[l], cb) ||
+        (t_new > 0 && overlap(beacons_out[l], bb, q_new[l], qb)))
+      return BKV_EALIAS;
+  }
+  FpsArgs a;
+  memset(&a, 0, sizeof(a));
+  a.batch = shape->batch;
+  a.n_q_heads = shape->n_q_heads;
+  a.n_kv_heads = shape->n_kv_heads;
+  a.group = g;
+  a.nb_max = nb_max;
+  a.q_len = q_len;
+  a.t_new = t_new;
+  for (int l0 = 0; l0 < shape->n_layers; l0 += kMaxLayers) {
+    const int nl = std::min(kMaxLayers, shape->n_layers - l0);
+    for (int i = 0; i < nl; ++i) {
+      a.beacons_in[i] = static_cast<const uint16_t*>(beacons_in[l0 + i]);
+      a.n_in[i] = n_in[l0 + i];
+      a.q_new[i] = t_new > 0 ? static_cast<const uint16_t*>(q_new[l0 + i]) : nullptr;
+      a.beacons_out[i] = static_cast<uint16_t*>(beacons_out[l0 + i]);
+      a.n_out[i] = n_out[l0 + i];
+    }
+    st = hip_status(launch_fps(a, nl, shape->head_dim, static_cast<int>(pool_max), stream));
+    if (st != BKV_OK) return st;
+  }
+  return BKV_OK;
+}
+
+size_t bkv_compress_workspace_bytes(const bkv_shape* shape, int32_t window, int32_t nb_max, int32_t budget) {
+  (void)budget;
+  return bkv_score_workspace_bytes(shape, window, nb_max);
+}
+
+bkv_status bkv_compress(const bkv_shape* shape, const void* const* k, const void* const* v, const void* const* q,
+                        int32_t q_len, int32_t window, const void* const* beacons, const int32_t* const* n_beacons,
+                        int32_t nb_max, int32_t budget, float* const* scores, int32_t* const* idx,
+                        int32_t* const* n_kept, void* const* k_out, void* const* v_out, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  bkv_status st = check_score_args(shape, k, q, q_len, window, beacons, n_beacons, nb_max, scores);
+  if (st == BKV_OK) st = check_select_args(shape, scores, budget, window, idx, n_kept);
+  if (st == BKV_OK) st = check_compact_args(shape, k, v, idx, n_kept, budget, k_out, v_out);
+  if (st != BKV_OK) return st;
+  st = bkv_score(shape, k, q, q_len, window, beacons, n_beacons, nb_max, scores, workspace, workspace_bytes, stream);
+  if (st != BKV_OK) return st;
+  st = bkv_select_topk(shape, scores, budget, window, idx, n_kept, nullptr, 0, stream);
+  if (st != BKV_OK) return st;
+  return bkv_compact(shape, k, v, idx, n_kept, budget, k_out, v_out, stream);
+}
+
+}  // extern "C"

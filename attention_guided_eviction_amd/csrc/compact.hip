@@ -1,0 +1,50 @@
+// Eviction by compaction (BeaconKV page, Abstract: only the selected KV pairs stay):
+// k_out[r] = k[idx[r]], v_out[r] = v[idx[r]] for r < n_kept, as bit copies.
+//
+// Each thread moves one 16-byte chunk of a K row and the same chunk of the V row, so a
+// wavefront reads and writes whole 256-byte rows (head_dim 128) contiguously.
+#include "bkv_internal.h"
+
+namespace bkv {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void compact_kernel(const CompactArgs a, int blocks_per_unit) {
+  constexpr int kChunks = D / 8;
+  const int u = blockIdx.x / blocks_per_unit;
+  const int blk = blockIdx.x - u * blocks_per_unit;
+  const int per_layer = a.batch * a.n_kv_heads;
+  const int layer = u / per_layer;
+  const int bh = u - layer * per_layer;
+  int n = a.n_kept[layer][bh];
+  n = n < 0 ? 0 : (n > a.budget ? a.budget : n);
+  const int c = blk * kThreads + threadIdx.x;
+  const int r = c / kChunks;
+  if (r >= n) return;
+  const int part = c - r * kChunks;
+  int src = a.idx[layer][static_cast<size_t>(bh) * a.budget + r];
+  src = src < 0 ? 0 : (src >= a.capacity ? a.capacity - 1 : src);
+  const size_t in_off = (static_cast<size_t>(bh) * a.capacity + src) * D + part * 8;
+  const size_t out_off = (static_cast<size_t>(bh) * a.budget + r) * D + part * 8;
+  const uint4 kv = *reinterpret_cast<const uint4*>(a.k[layer] + in_off);
+  const uint4 vv = *reinterpret_cast<const uint4*>(a.v[layer] + in_off);
+  *reinterpret_cast<uint4*>(a.k_out[layer] + out_off) = kv;
+  *reinterpret_cast<uint4*>(a.v_out[layer] + out_off) = vv;
+}
+
+}  // namespace
+
+hipError_t launch_compact(const CompactArgs& a, int n_layers, int head_dim, hipStream_t s) {
+  const long long chunks = static_cast<long long>(a.budget) * (head_dim / 8);
+  const int blocks_per_unit = static_cast<int>((chunks + kThreads - 1) / kThreads);
+  const unsigned grid = static_cast<unsigned>(n_layers) * a.batch * a.n_kv_heads * blocks_per_unit;
+  if (head_dim == 128)
+    hipLaunchKernelGGL(compact_kernel<128>, dim3(grid), dim3(kThreads), 0, s, a, blocks_per_unit);
+  else
+    hipLaunchKernelGGL(compact_kernel<64>, dim3(grid), dim3(kThreads), 0, s, a, blocks_per_unit);
+  return hipGetLastError();
+}
+
+}  // namespace bkv

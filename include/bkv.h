@@ -1,0 +1,221 @@
+/*
+ * bkv.h -- beacon-guided KV-cache compression on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libbkv.so.  The operations follow "BeaconKV: Key-Value Cache Compression
+ * Guided by Beacon Queries for Efficient Large Reasoning Model Inference"
+ * (thelatestinai.com/papers/2609.04971):
+ *
+ *   bkv_update_beacons  keeps per-KV-head beacon queries by continual farthest-point
+ *                       sampling (Figure 7 caption; Abstract: compact representatives of
+ *                       the global query clusters, no full query history);
+ *   bkv_score           attention-based score of every cached key from the recent queries
+ *                       and the beacon queries (Figure 5 (b)), max-aggregated over queries
+ *                       and heads (Figure 5 (c); Table 2 caption);
+ *   bkv_select_topk     top-K under the cache budget (Figure 5 (c)), the recent window
+ *                       always kept;
+ *   bkv_compact         eviction: the kept K/V rows gathered into a compacted cache
+ *                       (Abstract);
+ *   bkv_compress        bkv_score + bkv_select_topk + bkv_compact in one call.
+ *
+ * Conventions shared by every entry point
+ * ----------------------------------------
+ * Unit.  A unit is one (layer, sequence b, KV head h).  Query head h*G + r (r < G,
+ * G = n_q_heads / n_kv_heads) belongs to KV head h.
+ *
+ * Layers.  Every per-layer argument is a HOST array of shape->n_layers DEVICE pointers,
+ * one per layer, so one call covers a whole model.  The arrays are read during the call
+ * only.  Layer pointers may differ in anything but shape.
+ *
+ * Layouts (all row-major, contiguous, bf16 = raw IEEE bfloat16 bit patterns):
+ *   K, V cache     bf16  [batch][n_kv_heads][capacity][head_dim]
+ *   queries        bf16  [batch][n_q_heads][q_len][head_dim]   (newest query last)
+ *   beacons        bf16  [batch][n_kv_heads][nb_max][head_dim]
+ *   beacon counts  int32 [batch][n_kv_heads]
+ *   scores         fp32  [batch][n_kv_heads][capacity]
+ *   kept positions int32 [batch][n_kv_heads][budget]
+ *   kept counts    int32 [batch][n_kv_heads]
+ *   compacted K, V bf16  [batch][n_kv_heads][budget][head_dim]
+ * Row j of a cache is valid for j < L_b = min(seq_len[b], capacity).
+ *
+ * Memory and ordering.  Every pointer is device memory owned by the caller unless stated
+ * otherwise.  The library never allocates, frees or synchronises; it keeps no pointer
+ * after returning.  All work is enqueued on `stream` (0 = the null stream) and runs in
+ * stream order; results are visible after the caller synchronises.  Calls are
+ * thread-safe; concurrent calls must not share output or workspace buffers.
+ *
+ * Errors.  Arguments are checked on the host before anything is enqueued; a failing call
+ * enqueues nothing and returns a negative bkv_status.  Device-resident values are not
+ * errors: seq_len[b] is clamped to [0, capacity] and beacon counts to [0, nb_max] inside
+ * the kernels.  A failed launch returns BKV_EHIP (the stream may then hold part of the
+ * call's work).
+ */
+#ifndef BKV_H_
+#define BKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum bkv_status {
+  BKV_OK = 0,
+  BKV_EINVAL = -1,        /* null pointer, non-positive size, window > budget, ...     */
+  BKV_EUNSUPPORTED = -2,  /* valid but outside what the kernels support (head_dim,      */
+                          /* observation rows, beacon pool size)                        */
+  BKV_EALIAS = -3,        /* an output overlaps an input it must not overlap            */
+  BKV_EWORKSPACE = -4,    /* workspace missing or smaller than the *_workspace_bytes    */
+  BKV_EHIP = -5           /* a HIP launch or runtime call failed                        */
+} bkv_status;
+
+typedef struct bkv_shape {
+  int32_t n_layers;        /* >= 1: length of every per-layer pointer array             */
+  int32_t batch;           /* >= 1 sequences                                           */
+  int32_t n_q_heads;       /* >= 1, a multiple of n_kv_heads                             */
+  int32_t n_kv_heads;      /* >= 1                                                     */
+  int32_t head_dim;        /* 64 or 128                                                */
+  int32_t capacity;        /* >= 1 rows allocated per (sequence, KV head)               */
+  const int32_t* seq_len;  /* DEVICE int32 [batch]: valid rows per sequence (all layers) */
+} bkv_shape;
+
+/* Largest number of observation rows (n_q_heads/n_kv_heads * window + nb_max) that
+ * bkv_score / bkv_compress accept. */
+#define BKV_MAX_OBS 512
+/* Largest beacon pool (nb_max + n_q_heads/n_kv_heads * t_new) bkv_update_beacons accepts. */
+#define BKV_MAX_POOL 768
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* bkv_status_string(bkv_status status);
+
+/* Library version, e.g. "0.1.0" (static string). */
+const char* bkv_version(void);
+
+/* ------------------------------------------------------------------------------------
+ * Continual farthest-point sampling of beacon queries.
+ * BeaconKV page, Figure 7 caption ("Continual FPS") and Abstract (beacons are compact
+ * representatives of each global query cluster, maintained without the full query
+ * history); Figure 4 (a) measures query similarity by cosine similarity.
+ *
+ * Per unit, the candidate pool is the live beacons beacons_in[b][h][0 .. c) in stored
+ * order, c = clamp(n_in[b][h], 0, nb_max), followed by the new queries of the group's
+ * query heads h*G .. h*G+G-1, head-major, each head contributing its last t_new stored
+ * rows (of q_len) in time order.  If the pool has at most nb_max rows all of them are
+ * kept in pool order; otherwise nb_max rows are chosen greedily: first pool row 0, then
+ * repeatedly the not-yet-chosen row whose cosine distance (1 - cos) to its nearest chosen
+ * row is largest, ties to the lower pool index.  Distances are computed in fp32 from the
+ * bf16 rows.
+ *
+ * beacons_out[b][h][0 .. n_out) receive bit copies of the chosen rows in choice order;
+ * slots from n_out up are left untouched.  n_out[b][h] = min(nb_max, pool size).
+ *
+ * q_new:   per layer bf16 [batch][n_q_heads][q_len][head_dim]; 0 <= t_new <= q_len.
+ * n_in:    per layer int32 [batch][n_kv_heads].
+ * Errors:  BKV_EINVAL for null arrays/pointers or bad sizes; BKV_EUNSUPPORTED if
+ *          nb_max + G * t_new > BKV_MAX_POOL or head_dim is not 64/128; BKV_EALIAS if a
+ *          beacons_out layer overlaps the same layer's beacons_in or q_new.
+ * ---------------------------------------------------------------------------------- */
+bkv_status bkv_update_beacons(const bkv_shape* shape,
+                              const void* const* beacons_in, const int32_t* const* n_in,
+                              int32_t nb_max,
+                              const void* const* q_new, int32_t q_len, int32_t t_new,
+                              void* const* beacons_out, int32_t* const* n_out,
+                              hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * Attention-based key scores, max-aggregated.
+ * BeaconKV page, Figure 5 (b) (scores from beacon queries and recent queries),
+ * Figure 5 (c) and Table 2 caption (max aggregation across heads and queries).
+ *
+ * Per unit the observation set is, in this order, the last `window` stored queries of
+ * each query head of the group (head-major, time order) and the live beacons
+ * beacons[b][h][0 .. nb), nb = clamp(n_beacons[b][h], 0, nb_max).  With
+ * s_ij = q_i . k_j / sqrt(head_dim) (bf16 inputs, fp32 accumulation) and the softmax
+ * over all valid keys j < L_b (no causal mask), the score of key j is
+ *     scores[b][h][j] = max_i exp(s_ij - logsumexp_j' s_ij'),
+ * i.e. the largest attention weight any observation query gives it.  Entries j >= L_b
+ * are not written.  With an empty observation set every valid score is 0.
+ *
+ * window:      0 <= window <= q_len; n_q_heads/n_kv_heads * window + nb_max <= BKV_MAX_OBS.
+ * beacons, n_beacons: may be NULL arrays when nb_max == 0.
+ * workspace:   device scratch of at least bkv_score_workspace_bytes(...) bytes (256-byte
+ *              aligned), contents irrelevant on entry and undefined on exit.
+ * Errors:      BKV_EINVAL, BKV_EUNSUPPORTED (head_dim, observation rows), BKV_EWORKSPACE,
+ *              BKV_EALIAS if a scores layer overlaps that layer's K.
+ * ---------------------------------------------------------------------------------- */
+size_t bkv_score_workspace_bytes(const bkv_shape* shape, int32_t window, int32_t nb_max);
+
+bkv_status bkv_score(const bkv_shape* shape,
+                     const void* const* k,
+                     const void* const* q, int32_t q_len, int32_t window,
+                     const void* const* beacons, const int32_t* const* n_beacons, int32_t nb_max,
+                     float* const* scores,
+                     void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * Top-K selection under the budget with the recent window always kept.
+ * BeaconKV page, Figure 5 (c) (top-K selection via max aggregation of the scores).
+ *
+ * Per unit with L = L_b: if L <= budget every position 0 .. L-1 is kept.  Otherwise the
+ * last `window` positions L-window .. L-1 are kept, and the budget - window positions
+ * before them with the largest scores (compared as fp32; equal scores go to the lower
+ * position).  idx[b][h][0 .. n) receives the kept positions in ascending order and
+ * n_kept[b][h] = n = min(budget, L); idx slots from n up are left untouched.
+ * Scores must be non-negative (as bkv_score produces); NaN ordering is unspecified.
+ *
+ * 1 <= budget, 0 <= window <= budget.  workspace may be NULL when
+ * bkv_select_workspace_bytes(...) returns 0.
+ * Errors: BKV_EINVAL, BKV_EWORKSPACE, BKV_EALIAS if idx overlaps scores.
+ * ---------------------------------------------------------------------------------- */
+size_t bkv_select_workspace_bytes(const bkv_shape* shape, int32_t budget);
+
+bkv_status bkv_select_topk(const bkv_shape* shape,
+                           const float* const* scores, int32_t budget, int32_t window,
+                           int32_t* const* idx, int32_t* const* n_kept,
+                           void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * Eviction by compaction: kept rows gathered into a new cache.
+ * BeaconKV page, Abstract (the cache keeps only the selected KV pairs).
+ *
+ * For r < n = clamp(n_kept[b][h], 0, budget):
+ *     k_out[b][h][r] = k[b][h][idx[b][h][r]],  v_out[b][h][r] = v[b][h][idx[b][h][r]]
+ * as bit copies; rows from n up are left untouched.  Positions outside [0, capacity) are
+ * clamped into it (bkv_select_topk never produces them).  Out of place: outputs must not
+ * overlap K or V.
+ * Errors: BKV_EINVAL, BKV_EUNSUPPORTED (head_dim), BKV_EALIAS.
+ * ---------------------------------------------------------------------------------- */
+bkv_status bkv_compact(const bkv_shape* shape,
+                       const void* const* k, const void* const* v,
+                       const int32_t* const* idx, const int32_t* const* n_kept, int32_t budget,
+                       void* const* k_out, void* const* v_out,
+                       hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * One compression event: bkv_score, then bkv_select_topk, then bkv_compact, with the
+ * arguments of those three calls (same meaning, same errors).  Writes scores, idx,
+ * n_kept, k_out and v_out exactly as the three calls would.
+ * workspace: at least bkv_compress_workspace_bytes(...) bytes.
+ * ---------------------------------------------------------------------------------- */
+size_t bkv_compress_workspace_bytes(const bkv_shape* shape, int32_t window, int32_t nb_max,
+                                    int32_t budget);
+
+bkv_status bkv_compress(const bkv_shape* shape,
+                        const void* const* k, const void* const* v,
+                        const void* const* q, int32_t q_len, int32_t window,
+                        const void* const* beacons, const int32_t* const* n_beacons, int32_t nb_max,
+                        int32_t budget,
+                        float* const* scores, int32_t* const* idx, int32_t* const* n_kept,
+                        void* const* k_out, void* const* v_out,
+                        void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+#ifdef __cplusplus
+}  /* extern "C" */
+#endif
+
+#endif  /* BKV_H_ */

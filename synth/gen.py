@@ -77,6 +77,7 @@ class Workload:
     seg_mean: float = 64.0        # mean key-segment length
     spread: float = 0.3           # RMS-per-coordinate deviation around a scaled centre
     seed: int = 0
+    lengths: Optional[tuple] = None   # explicit per-sequence lengths (edge-case workloads)
 
     @property
     def group(self) -> int:
@@ -195,6 +196,8 @@ def _rng(*fields: int) -> np.random.Generator:
 
 def seq_lengths(w: Workload) -> np.ndarray:
     """Valid cached keys per sequence (int32 [batch])."""
+    if w.lengths is not None:
+        return np.asarray(w.lengths, dtype=np.int32)
     if w.ragged is None:
         return np.full(w.batch, w.seq_len, dtype=np.int32)
     lo, hi = w.ragged

@@ -1,0 +1,151 @@
+"""The C ABI: the library loads, exports every entry point include/bkv.h declares, and
+rejects bad arguments on the host before touching the GPU.  CPU only: every call here
+fails validation (fake device addresses are never dereferenced)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from attention_guided_eviction_amd import bkv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bkv.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bkv_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_binding_exports():
+    assert _declared() == sorted(bkv.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = bkv.load()
+    nm = subprocess.run(["nm", "-D", "--defined-only", bkv.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (bkv_\w+)", nm))
+    for name in _declared():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_status_strings_and_version():
+    for code in (0, -1, -2, -3, -4, -5):
+        assert bkv.status_string(code).startswith("BKV_")
+    assert "unknown" in bkv.status_string(7)
+    assert re.match(r"\d+\.\d+\.\d+$", bkv.version())
+
+
+def test_header_limits_match_binding():
+    text = open(HEADER).read()
+    assert int(re.search(r"#define BKV_MAX_OBS (\d+)", text).group(1)) == bkv.MAX_OBS
+    assert int(re.search(r"#define BKV_MAX_POOL (\d+)", text).group(1)) == bkv.MAX_POOL
+
+
+# ------------------------------------------------------------------------------------------------
+# host-side validation with fake addresses
+# ------------------------------------------------------------------------------------------------
+
+FAKE = 0x7F0000000000
+
+
+def shape(**kw):
+    d = dict(n_layers=2, batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, capacity=1024, seq_len=FAKE)
+    d.update(kw)
+    return bkv._Shape(d["n_layers"], d["batch"], d["n_q_heads"], d["n_kv_heads"], d["head_dim"], d["capacity"],
+                      d["seq_len"])
+
+
+def arr(base, n=2, stride=1 << 32):
+    return (ctypes.c_void_p * n)(*[base + i * stride for i in range(n)])
+
+
+def nulls(n=2):
+    return (ctypes.c_void_p * n)(*([None] * n))
+
+
+def score_call(s=None, k=None, q=None, q_len=32, window=32, bc=None, nb=None, nb_max=16, sc=None, ws=FAKE + (1 << 40),
+               ws_bytes=1 << 40):
+    lib = bkv.load()
+    s = s or shape()
+    return lib.bkv_score(ctypes.byref(s), k or arr(FAKE + (1 << 36)), q or arr(FAKE + (2 << 36)), q_len, window,
+                         bc or arr(FAKE + (3 << 36)), nb or arr(FAKE + (4 << 36)), nb_max, sc or arr(FAKE + (5 << 36)),
+                         ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(s=shape(head_dim=96)), bkv.BKV_EUNSUPPORTED),
+    (dict(s=shape(head_dim=0)), bkv.BKV_EINVAL),
+    (dict(s=shape(n_q_heads=6, n_kv_heads=4)), bkv.BKV_EINVAL),
+    (dict(s=shape(seq_len=0)), bkv.BKV_EINVAL),
+    (dict(s=shape(n_layers=0)), bkv.BKV_EINVAL),
+    (dict(s=shape(capacity=0)), bkv.BKV_EINVAL),
+    (dict(window=33), bkv.BKV_EINVAL),
+    (dict(window=-1), bkv.BKV_EINVAL),
+    (dict(nb_max=-1), bkv.BKV_EINVAL),
+    (dict(k=nulls()), bkv.BKV_EINVAL),
+    (dict(sc=nulls()), bkv.BKV_EINVAL),
+    (dict(bc=nulls()), bkv.BKV_EINVAL),
+    (dict(window=32, q_len=200, nb_max=400), bkv.BKV_EUNSUPPORTED),   # 4*32 + 400 > 512 rows
+    (dict(ws=None), bkv.BKV_EWORKSPACE),
+    (dict(ws_bytes=16), bkv.BKV_EWORKSPACE),
+    (dict(ws=FAKE + (1 << 40) + 8), bkv.BKV_EWORKSPACE),              # misaligned
+    (dict(sc=arr(FAKE + (1 << 36) + 4096)), bkv.BKV_EALIAS),          # scores inside K
+])
+def test_score_rejects(kw, status):
+    assert score_call(**kw) == status
+
+
+def test_workspace_bytes_monotone():
+    lib = bkv.load()
+    a = lib.bkv_score_workspace_bytes(ctypes.byref(shape()), 32, 16)
+    b = lib.bkv_score_workspace_bytes(ctypes.byref(shape(capacity=4096)), 32, 16)
+    c = lib.bkv_score_workspace_bytes(ctypes.byref(shape(capacity=4096)), 64, 16)
+    assert 0 < a < b < c
+    assert lib.bkv_score_workspace_bytes(ctypes.byref(shape(head_dim=96)), 32, 16) == 0
+    assert lib.bkv_compress_workspace_bytes(ctypes.byref(shape()), 32, 16, 256) >= a
+
+
+def test_select_rejects():
+    lib = bkv.load()
+    s = shape()
+    sc, idx, nk = arr(FAKE), arr(FAKE + (1 << 36)), arr(FAKE + (2 << 36))
+    assert lib.bkv_select_topk(ctypes.byref(s), sc, 0, 0, idx, nk, None, 0, None) == bkv.BKV_EINVAL
+    assert lib.bkv_select_topk(ctypes.byref(s), sc, 64, 65, idx, nk, None, 0, None) == bkv.BKV_EINVAL
+    assert lib.bkv_select_topk(ctypes.byref(s), nulls(), 64, 8, idx, nk, None, 0, None) == bkv.BKV_EINVAL
+    assert lib.bkv_select_topk(ctypes.byref(shape(capacity=70000)), sc, 64, 8, idx, nk, None, 0,
+                               None) == bkv.BKV_EUNSUPPORTED
+    assert lib.bkv_select_topk(ctypes.byref(s), sc, 64, 8, arr(FAKE + 64), nk, None, 0, None) == bkv.BKV_EALIAS
+
+
+def test_compact_rejects_aliasing():
+    lib = bkv.load()
+    s = shape()
+    k, v = arr(FAKE), arr(FAKE + (1 << 36))
+    idx, nk = arr(FAKE + (2 << 36)), arr(FAKE + (3 << 36))
+    ko, vo = arr(FAKE + (4 << 36)), arr(FAKE + (5 << 36))
+    assert lib.bkv_compact(ctypes.byref(s), k, v, idx, nk, 0, ko, vo, None) == bkv.BKV_EINVAL
+    assert lib.bkv_compact(ctypes.byref(s), k, v, idx, nk, 64, arr(FAKE + 256), vo, None) == bkv.BKV_EALIAS
+    assert lib.bkv_compact(ctypes.byref(s), k, v, idx, nk, 64, ko, arr(FAKE + (1 << 36)), None) == bkv.BKV_EALIAS
+    assert lib.bkv_compact(ctypes.byref(s), k, v, idx, nk, 64, ko, ko, None) == bkv.BKV_EALIAS
+    assert lib.bkv_compact(ctypes.byref(s), k, nulls(), idx, nk, 64, ko, vo, None) == bkv.BKV_EINVAL
+
+
+def test_update_beacons_rejects():
+    lib = bkv.load()
+    s = shape()
+    bi, ni, qn = arr(FAKE), arr(FAKE + (1 << 36)), arr(FAKE + (2 << 36))
+    bo, no = arr(FAKE + (3 << 36)), arr(FAKE + (4 << 36))
+    f = lib.bkv_update_beacons
+    assert f(ctypes.byref(s), bi, ni, 0, qn, 128, 128, bo, no, None) == bkv.BKV_EINVAL       # nb_max < 1
+    assert f(ctypes.byref(s), bi, ni, 16, qn, 128, 129, bo, no, None) == bkv.BKV_EINVAL     # t_new > q_len
+    assert f(ctypes.byref(s), bi, ni, 16, qn, 256, 256, bo, no, None) == bkv.BKV_EUNSUPPORTED  # pool 16+4*256
+    assert f(ctypes.byref(s), bi, ni, 16, qn, 128, 128, bi, no, None) == bkv.BKV_EALIAS
+    assert f(ctypes.byref(s), bi, ni, 16, qn, 128, 128, bo, ni, None) == bkv.BKV_EALIAS
+    assert f(ctypes.byref(s), bi, ni, 16, qn, 128, 128, qn, no, None) == bkv.BKV_EALIAS
+    assert f(ctypes.byref(s), bi, ni, 16, nulls(), 128, 128, bo, no, None) == bkv.BKV_EINVAL
+    assert f(ctypes.byref(shape(head_dim=32)), bi, ni, 16, qn, 128, 128, bo, no, None) == bkv.BKV_EUNSUPPORTED

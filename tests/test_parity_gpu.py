@@ -1,0 +1,79 @@
+"""GPU parity against the CPU oracle, every unit checked, on workloads small enough for
+the oracle: the tiny workload at full size, the four model-shaped workloads with fewer
+layers and shorter caches (still many tiles and ragged tails), and edge cases."""
+import pytest
+import torch
+
+from synth import WORKLOADS
+from parity import all_units, check_units, log, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_all(w):
+    log(f"[parity] {w.name}: layers {w.n_layers} batch {w.batch} cap {w.capacity} window {w.window} "
+        f"nb {w.nb_init}/{w.nb_max} budget {w.budget} t_new {w.t_new}")
+    ev, _ = run_gpu(w)
+    worst = check_units(w, ev, all_units(w))
+    log(f"[parity] {w.name}: worst {worst}")
+    return worst
+
+
+def test_tiny_full_size():
+    _run_all(WORKLOADS["tiny"])
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("qwen7b_16k", dict(n_layers=2, capacity=3000, seq_len=2989, budget=700)),
+    ("llama8b_32k", dict(n_layers=1, batch=2, capacity=2304, seq_len=2304, budget=512)),
+    ("qwen14b_64k", dict(n_layers=1, batch=1, capacity=4096, seq_len=4001, budget=1024)),
+    ("qwen4b_serving", dict(n_layers=1, batch=3, capacity=2048, ragged=(700, 2048), budget=400)),
+])
+def test_model_shapes_reduced(name, kw):
+    _run_all(WORKLOADS[name].replace(name=name + "_reduced", **kw))
+
+
+EDGE = {
+    # lengths around the budget, the window and tile edges; an empty sequence
+    "lengths": WORKLOADS["tiny"].replace(batch=8, capacity=700,
+                                         lengths=(0, 5, 127, 128, 129, 257, 511, 700), t_new=0),
+    # head_dim 128, no beacons, no window: recent-only is empty, scores all zero
+    "no_observers": WORKLOADS["tiny"].replace(head_dim=128, window=0, nb_init=0, nb_max=0, t_new=0,
+                                              capacity=300, seq_len=300),
+    # window only (recent-query scoring, n_beacon = 0)
+    "recent_only": WORKLOADS["tiny"].replace(nb_init=0, nb_max=0, t_new=0, capacity=1000, seq_len=999),
+    # beacons only, partial live count
+    "beacons_only": WORKLOADS["tiny"].replace(window=0, nb_init=3, nb_max=8, t_new=0, capacity=600, seq_len=600,
+                                              budget=64),
+    # largest observation set: 4 * 120 + 32 = 512 rows
+    "max_obs": WORKLOADS["qwen7b_16k"].replace(n_layers=1, n_q_heads=16, n_kv_heads=4, window=120, nb_init=32,
+                                               nb_max=32, capacity=1500, seq_len=1500, budget=600),
+    # window equals budget: nothing chosen by score
+    "window_eq_budget": WORKLOADS["tiny"].replace(window=8, budget=8, t_new=0, capacity=400, seq_len=400),
+    # more layers than one launch holds (48)
+    "many_layers": WORKLOADS["tiny"].replace(n_layers=50, capacity=256, seq_len=250, budget=64, t_new=0),
+    # FPS: pool smaller than capacity (copy path), then t_new < q_len
+    "fps_small_pool": WORKLOADS["tiny"].replace(nb_init=2, nb_max=32, t_new=8),
+    "fps_partial_new": WORKLOADS["qwen4b_serving"].replace(n_layers=1, batch=2, capacity=1024, ragged=(600, 1024),
+                                                           t_new=48, window=16, budget=256, nb_init=5),
+    "fps_empty_beacons": WORKLOADS["qwen4b_serving"].replace(n_layers=1, batch=2, capacity=512, ragged=(300, 512),
+                                                             nb_init=0, budget=128),
+}
+
+
+@pytest.mark.parametrize("case", sorted(EDGE))
+def test_edge_cases(case):
+    _run_all(EDGE[case].replace(name=case))
+
+
+def test_identical_keys_tie_to_lowest_positions():
+    """All keys equal: every score is 1/L and the kept prefix is the lowest positions."""
+    w = WORKLOADS["tiny"].replace(name="ties", t_new=0, capacity=512, seq_len=512)
+    from parity import build_inputs, check_units
+    inp = build_inputs(w)
+    inp["k"][0][:] = inp["k"][0][0, 0, 0]
+    ev, _ = run_gpu(w, inp)
+    idx = ev.idx[0][0, 0].cpu().tolist()
+    assert idx == list(range(w.budget - w.window)) + list(range(512 - w.window, 512))
+    s = ev.scores[0][0, 0].cpu()
+    assert torch.allclose(s, torch.full_like(s, 1 / 512), rtol=1e-5)
