@@ -55,9 +55,11 @@ size_t layer_bytes(const bkv_shape* s, int heads, long long rows, long long cols
   return n;
 }
 
+// Observation rows per unit rounded up to whole 32-row MFMA blocks (at least one block,
+// so the workspace is never empty).
 int obs_pad_of(const bkv_shape* s, int window, int nb_max) {
   const int g = s->n_q_heads / s->n_kv_heads;
-  return round_up(g * window + nb_max, 32);
+  return std::max(32, round_up(g * window + nb_max, 32));
 }
 
 int layers_per_launch(const bkv_shape* s) { return std::min(s->n_layers, kMaxLayers); }

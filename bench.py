@@ -1,0 +1,212 @@
+#!/usr/bin/env python3
+"""Benchmark: one compression event per step over every layer of a model-shaped KV cache.
+
+A step is the whole path for one batch of synthetic input already resident in HBM:
+(beacon update when the workload has one,) scoring, top-K selection and compaction of
+every (layer, sequence, KV head).  Default workload: R1-Distill-Qwen-7B attention
+geometry, 28 layers, 28 query / 4 KV heads, head_dim 128, one 16,384-token trace,
+window 32, 16 beacons per KV head, budget 4096.
+
+Prints one JSON line (rank 0, one GPU):
+  value       cached KV tokens compressed per second (sum over sequences of L_b per step,
+              a token counted once across layers and heads)
+  roofline    the dominant kernel group's algorithmic bytes / measured duration vs 8 TB/s
+  cpu_baseline  the float64 CPU oracle on a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="qwen7b_16k")
+    p.add_argument("--cpu-units", type=int, default=32, help="units in the CPU-oracle sample (0: skip)")
+    p.add_argument("--quiet", action="store_true")
+    return p.parse_args()
+
+
+def alg_bytes(w, lens):
+    """Algorithmic HBM bytes of one event per kernel group: K rows read once and the
+    observation queries (score), scores read and positions written (select), kept K/V rows
+    read and written plus positions (compact), pool read and beacons written (fps)."""
+    D, G = w.head_dim, w.group
+    n_obs = G * w.window + w.nb_max
+    per_layer_heads = w.n_kv_heads
+    score = select = compact = fps = 0
+    for L in lens:
+        L = int(L)
+        N = min(w.budget, L)
+        u = w.n_layers * per_layer_heads
+        score += u * (L * D * 2 + n_obs * D * 2)
+        select += u * (L * 4 + N * 4)
+        compact += u * (4 * N * D * 2 + N * 4)
+        if w.runs_fps:
+            fps += u * ((w.nb_init + G * w.t_new) * D * 2 + w.nb_max * D * 2)
+    return {"score": score, "select": select, "compact": compact, "fps": fps}
+
+
+def score_flops(w, lens):
+    n_obs = w.group * w.window + w.nb_max
+    return sum(2.0 * n_obs * int(L) * w.head_dim * w.n_layers * w.n_kv_heads for L in lens)
+
+
+def cpu_baseline(w, n_units):
+    """Time the CPU oracle on a bounded sample of units of the same workload."""
+    import numpy as np
+    import threadpoolctl
+    from synth import unit_inputs, bf16_bits, seq_lengths
+    from oracle import bkv_oracle as O
+    rng = np.random.default_rng(1)
+    lens = seq_lengths(w)
+    units = [(int(rng.integers(w.n_layers)), int(rng.integers(w.batch)), int(rng.integers(w.n_kv_heads)))
+             for _ in range(n_units)]
+    t_total = 0.0
+    keys_total = 0
+    for (l, b, h) in units:
+        u = unit_inputs(w, l, b, h, "cpu")
+        kb, vb, qb, bb = bf16_bits(u["k"]), bf16_bits(u["v"]), bf16_bits(u["q"]), bf16_bits(u["beacons"])
+        t0 = time.perf_counter()
+        nb = u["nb"]
+        if w.runs_fps:
+            bb, nb, _ = O.update_beacons(bb, nb, qb[:, w.q_len - w.t_new:], w.nb_max)
+        O.compress_unit(kb, vb, qb, bb, nb, w.window, w.budget)
+        t_total += time.perf_counter() - t0
+        keys_total += u["L"]
+    # tokens/s: a token is compressed once all layers x KV heads of its sequence are done
+    rows_per_s = keys_total / t_total
+    tokens_per_s = rows_per_s / (w.n_layers * w.n_kv_heads)
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    return {"value": tokens_per_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_units} random (layer, sequence, KV head) units of {w.name}, "
+                      f"{keys_total} cached rows, {t_total:.1f} s of float64 NumPy "
+                      f"(beacon update, scores, top-K, compaction); scaled by layers x KV heads"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path shards by "
+              f"(layer, sequence, KV head) with no exchange)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from synth import WORKLOADS, seq_lengths
+    from attention_guided_eviction_amd import bkv
+    from attention_guided_eviction_amd.event import CompressionEvent, EventConfig
+
+    def log(*a):
+        if not args.quiet:
+            print(*a, file=sys.stderr, flush=True)
+
+    w = WORKLOADS[args.workload]
+    bkv.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    from synth import layer_tensors
+    layers = [layer_tensors(w, l, dev) for l in range(w.n_layers)]
+    inp = {key: [lt[key] for lt in layers] for key in layers[0]}
+    lens = seq_lengths(w)
+    seq_len = torch.from_numpy(lens).to(dev)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs for {w.name} built in {time.time() - t0:.1f}s")
+    cfg = EventConfig(w.n_layers, w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.capacity, w.q_len, w.window,
+                      w.nb_max, w.budget, w.t_new)
+    ev = CompressionEvent(cfg, seq_len, dev)
+    stream = torch.cuda.current_stream()
+    k, v, q, bc, nb = inp["k"], inp["v"], inp["q"], inp["beacons"], inp["n_beacons"]
+
+    for _ in range(args.warmup):
+        ev.run(k, v, q, bc, nb)
+    torch.cuda.synchronize()
+
+    # whole steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        ev.run(k, v, q, bc, nb)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    log(f"[bench] {args.steps} steps, {ms:.3f} ms/step")
+
+    # per-call durations, same stream, same inputs (separate timed loop)
+    scores_bc = ev.beacons_out if w.runs_fps else bc
+    scores_nb = ev.n_beacons_out if w.runs_fps else nb
+    calls = {}
+    if w.runs_fps:
+        calls["fps"] = lambda: ev.update_beacons(bc, nb, q)
+    calls["score"] = lambda: bkv.score(ev.shape, k, q, w.q_len, w.window, scores_bc, scores_nb, w.nb_max, ev.scores,
+                                       ev.workspace)
+    calls["select"] = lambda: bkv.select_topk(ev.shape, ev.scores, w.budget, w.window, ev.idx, ev.n_kept)
+    calls["compact"] = lambda: bkv.compact(ev.shape, k, v, ev.idx, ev.n_kept, w.budget, ev.k_out, ev.v_out)
+    per = {name: 0.0 for name in calls}
+    for _ in range(args.steps):
+        for name, fn in calls.items():
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            b.synchronize()
+            per[name] += a.elapsed_time(b)
+    per = {n: t / args.steps for n, t in per.items()}
+    log("[bench] per call ms: " + ", ".join(f"{n} {t:.3f}" for n, t in per.items()))
+
+    tokens = float(lens.sum())
+    ab = alg_bytes(w, lens)
+    total_bytes = sum(ab.values())
+    dom = max(per, key=per.get)
+    achieved = ab[dom] / (per[dom] * 1e-3) / 1e9
+    roof = {"kernel": {"score": "score_pass1 + score_merge + score_pass2 (bkv_score)",
+                       "select": "select_topk_kernel (bkv_select_topk)",
+                       "compact": "compact_kernel (bkv_compact)",
+                       "fps": "fps_kernel (bkv_update_beacons)"}[dom],
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "ms_per_launch": round(per[dom], 4), "alg_bytes_per_launch": ab[dom]}
+    if dom == "score":
+        tf = score_flops(w, lens) / (per[dom] * 1e-3) / 1e12
+        roof["mfma_tflops_one_pass"] = round(tf, 1)
+    out = {
+        "metric": "cached KV tokens compressed/sec per GPU; achieved HBM GB/s as % of peak",
+        "value": round(tokens / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "layers": w.n_layers, "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads,
+                   "head_dim": w.head_dim, "batch": w.batch, "seq_len": int(lens.max()) if w.ragged is None
+                   else f"ragged {w.ragged[0]}-{w.ragged[1]} (sum {int(lens.sum())})",
+                   "window": w.window, "beacons": w.nb_max, "budget": w.budget, "beacon_update_queries": w.t_new},
+        "hbm_alg_gbs": round(total_bytes / (ms * 1e-3) / 1e9, 1),
+        "hbm_alg_frac_of_peak": round(total_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "per_call_ms": {n: round(t, 4) for n, t in per.items()},
+        "roofline": roof,
+    }
+    if args.cpu_units > 0:
+        log(f"[bench] CPU oracle on {args.cpu_units} units ...")
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_units)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
