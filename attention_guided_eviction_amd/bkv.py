@@ -160,10 +160,23 @@ def _workspace(ws: Optional[torch.Tensor], need: int):
 
 
 # ------------------------------------------------------------------------------------------------
+# Each operation is split into prepare_*() -- checks every tensor once and builds the ctypes
+# argument list -- and a call of the returned object with an optional stream, so repeated
+# events over the same buffers pay the Python checks once.
 
-def update_beacons(s: CacheShape, beacons_in, n_in, nb_max: int, q_new, q_len: int, t_new: int,
-                   beacons_out, n_out, stream=None) -> None:
-    """Continual FPS update of the beacon sets of every layer (bkv_update_beacons)."""
+class Call:
+    """A prepared library call: `call(stream=None)` enqueues it on `stream` (default: the
+    current torch stream) and raises BkvError on a non-zero status."""
+
+    def __init__(self, fn, args, what: str, keep):
+        self._fn, self._args, self.what, self._keep = fn, args, what, keep
+
+    def __call__(self, stream=None) -> None:
+        _ok(self._fn(*self._args, _stream(stream)), self.what)
+
+
+def prepare_update_beacons(s: CacheShape, beacons_in, n_in, nb_max: int, q_new, q_len: int, t_new: int,
+                           beacons_out, n_out) -> Call:
     lib = load()
     B, Hq, Hkv, D, n = s.batch, s.n_q_heads, s.n_kv_heads, s.head_dim, s.n_layers
     shape = s.c()
@@ -172,8 +185,15 @@ def update_beacons(s: CacheShape, beacons_in, n_in, nb_max: int, q_new, q_len: i
     qn = _layers(q_new, n, torch.bfloat16, (B, Hq, q_len, D), "q_new") if t_new > 0 else _null_layers(n)
     bo = _layers(beacons_out, n, torch.bfloat16, (B, Hkv, nb_max, D), "beacons_out")
     no = _layers(n_out, n, torch.int32, (B, Hkv), "n_out")
-    _ok(lib.bkv_update_beacons(ctypes.byref(shape), bi, ni, nb_max, qn, q_len, t_new, bo, no, _stream(stream)),
-        "bkv_update_beacons")
+    args = (ctypes.byref(shape), bi, ni, nb_max, qn, q_len, t_new, bo, no)
+    return Call(lib.bkv_update_beacons, args, "bkv_update_beacons",
+                (shape, s.seq_len, beacons_in, n_in, q_new, beacons_out, n_out))
+
+
+def update_beacons(s: CacheShape, beacons_in, n_in, nb_max: int, q_new, q_len: int, t_new: int,
+                   beacons_out, n_out, stream=None) -> None:
+    """Continual FPS update of the beacon sets of every layer (bkv_update_beacons)."""
+    prepare_update_beacons(s, beacons_in, n_in, nb_max, q_new, q_len, t_new, beacons_out, n_out)(stream)
 
 
 def score_workspace_bytes(s: CacheShape, window: int, nb_max: int) -> int:
@@ -185,12 +205,8 @@ def alloc_workspace(nbytes: int, device="cuda") -> torch.Tensor:
     return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
 
 
-def score(s: CacheShape, k, q, q_len: int, window: int, beacons, n_beacons, nb_max: int, scores,
-          workspace: Optional[torch.Tensor], stream=None) -> None:
-    """Max-aggregated attention scores of every cached key (bkv_score)."""
-    lib = load()
+def _score_inputs(s: CacheShape, k, q, q_len, window, beacons, n_beacons, nb_max):
     B, Hq, Hkv, D, cap, n = s.batch, s.n_q_heads, s.n_kv_heads, s.head_dim, s.capacity, s.n_layers
-    shape = s.c()
     kp = _layers(k, n, torch.bfloat16, (B, Hkv, cap, D), "k")
     qp = _layers(q, n, torch.bfloat16, (B, Hq, q_len, D), "q") if window > 0 else _null_layers(n)
     if nb_max > 0:
@@ -198,26 +214,43 @@ def score(s: CacheShape, k, q, q_len: int, window: int, beacons, n_beacons, nb_m
         nbp = _layers(n_beacons, n, torch.int32, (B, Hkv), "n_beacons")
     else:
         bp, nbp = _null_layers(n), _null_layers(n)
-    sp = _layers(scores, n, torch.float32, (B, Hkv, cap), "scores")
+    return kp, qp, bp, nbp
+
+
+def prepare_score(s: CacheShape, k, q, q_len: int, window: int, beacons, n_beacons, nb_max: int, scores,
+                  workspace: Optional[torch.Tensor]) -> Call:
+    lib = load()
+    shape = s.c()
+    kp, qp, bp, nbp = _score_inputs(s, k, q, q_len, window, beacons, n_beacons, nb_max)
+    sp = _layers(scores, s.n_layers, torch.float32, (s.batch, s.n_kv_heads, s.capacity), "scores")
     wp, wn = _workspace(workspace, int(lib.bkv_score_workspace_bytes(ctypes.byref(shape), window, nb_max)))
-    _ok(lib.bkv_score(ctypes.byref(shape), kp, qp, q_len, window, bp, nbp, nb_max, sp, wp, wn, _stream(stream)),
-        "bkv_score")
+    args = (ctypes.byref(shape), kp, qp, q_len, window, bp, nbp, nb_max, sp, wp, wn)
+    return Call(lib.bkv_score, args, "bkv_score", (shape, s.seq_len, k, q, beacons, n_beacons, scores, workspace))
 
 
-def select_topk(s: CacheShape, scores, budget: int, window: int, idx, n_kept, stream=None) -> None:
-    """Top-K positions per KV head, window always kept, ascending (bkv_select_topk)."""
+def score(s: CacheShape, k, q, q_len: int, window: int, beacons, n_beacons, nb_max: int, scores,
+          workspace: Optional[torch.Tensor], stream=None) -> None:
+    """Max-aggregated attention scores of every cached key (bkv_score)."""
+    prepare_score(s, k, q, q_len, window, beacons, n_beacons, nb_max, scores, workspace)(stream)
+
+
+def prepare_select_topk(s: CacheShape, scores, budget: int, window: int, idx, n_kept) -> Call:
     lib = load()
     B, Hkv, cap, n = s.batch, s.n_kv_heads, s.capacity, s.n_layers
     shape = s.c()
     sp = _layers(scores, n, torch.float32, (B, Hkv, cap), "scores")
     ip = _layers(idx, n, torch.int32, (B, Hkv, budget), "idx")
     np_ = _layers(n_kept, n, torch.int32, (B, Hkv), "n_kept")
-    _ok(lib.bkv_select_topk(ctypes.byref(shape), sp, budget, window, ip, np_, None, 0, _stream(stream)),
-        "bkv_select_topk")
+    args = (ctypes.byref(shape), sp, budget, window, ip, np_, None, 0)
+    return Call(lib.bkv_select_topk, args, "bkv_select_topk", (shape, s.seq_len, scores, idx, n_kept))
 
 
-def compact(s: CacheShape, k, v, idx, n_kept, budget: int, k_out, v_out, stream=None) -> None:
-    """Gather the kept K/V rows into compacted caches (bkv_compact)."""
+def select_topk(s: CacheShape, scores, budget: int, window: int, idx, n_kept, stream=None) -> None:
+    """Top-K positions per KV head, window always kept, ascending (bkv_select_topk)."""
+    prepare_select_topk(s, scores, budget, window, idx, n_kept)(stream)
+
+
+def prepare_compact(s: CacheShape, k, v, idx, n_kept, budget: int, k_out, v_out) -> Call:
     lib = load()
     B, Hkv, D, cap, n = s.batch, s.n_kv_heads, s.head_dim, s.capacity, s.n_layers
     shape = s.c()
@@ -227,27 +260,26 @@ def compact(s: CacheShape, k, v, idx, n_kept, budget: int, k_out, v_out, stream=
     np_ = _layers(n_kept, n, torch.int32, (B, Hkv), "n_kept")
     ko = _layers(k_out, n, torch.bfloat16, (B, Hkv, budget, D), "k_out")
     vo = _layers(v_out, n, torch.bfloat16, (B, Hkv, budget, D), "v_out")
-    _ok(lib.bkv_compact(ctypes.byref(shape), kp, vp, ip, np_, budget, ko, vo, _stream(stream)), "bkv_compact")
+    args = (ctypes.byref(shape), kp, vp, ip, np_, budget, ko, vo)
+    return Call(lib.bkv_compact, args, "bkv_compact", (shape, s.seq_len, k, v, idx, n_kept, k_out, v_out))
+
+
+def compact(s: CacheShape, k, v, idx, n_kept, budget: int, k_out, v_out, stream=None) -> None:
+    """Gather the kept K/V rows into compacted caches (bkv_compact)."""
+    prepare_compact(s, k, v, idx, n_kept, budget, k_out, v_out)(stream)
 
 
 def compress_workspace_bytes(s: CacheShape, window: int, nb_max: int, budget: int) -> int:
     return int(load().bkv_compress_workspace_bytes(ctypes.byref(s.c()), window, nb_max, budget))
 
 
-def compress(s: CacheShape, k, v, q, q_len: int, window: int, beacons, n_beacons, nb_max: int, budget: int,
-             scores, idx, n_kept, k_out, v_out, workspace: Optional[torch.Tensor], stream=None) -> None:
-    """One compression event over every layer: score, select, compact (bkv_compress)."""
+def prepare_compress(s: CacheShape, k, v, q, q_len: int, window: int, beacons, n_beacons, nb_max: int,
+                     budget: int, scores, idx, n_kept, k_out, v_out, workspace: Optional[torch.Tensor]) -> Call:
     lib = load()
-    B, Hq, Hkv, D, cap, n = s.batch, s.n_q_heads, s.n_kv_heads, s.head_dim, s.capacity, s.n_layers
+    B, Hkv, D, cap, n = s.batch, s.n_kv_heads, s.head_dim, s.capacity, s.n_layers
     shape = s.c()
-    kp = _layers(k, n, torch.bfloat16, (B, Hkv, cap, D), "k")
+    kp, qp, bp, nbp = _score_inputs(s, k, q, q_len, window, beacons, n_beacons, nb_max)
     vp = _layers(v, n, torch.bfloat16, (B, Hkv, cap, D), "v")
-    qp = _layers(q, n, torch.bfloat16, (B, Hq, q_len, D), "q") if window > 0 else _null_layers(n)
-    if nb_max > 0:
-        bp = _layers(beacons, n, torch.bfloat16, (B, Hkv, nb_max, D), "beacons")
-        nbp = _layers(n_beacons, n, torch.int32, (B, Hkv), "n_beacons")
-    else:
-        bp, nbp = _null_layers(n), _null_layers(n)
     sp = _layers(scores, n, torch.float32, (B, Hkv, cap), "scores")
     ip = _layers(idx, n, torch.int32, (B, Hkv, budget), "idx")
     np_ = _layers(n_kept, n, torch.int32, (B, Hkv), "n_kept")
@@ -255,5 +287,13 @@ def compress(s: CacheShape, k, v, q, q_len: int, window: int, beacons, n_beacons
     vo = _layers(v_out, n, torch.bfloat16, (B, Hkv, budget, D), "v_out")
     need = int(lib.bkv_compress_workspace_bytes(ctypes.byref(shape), window, nb_max, budget))
     wp, wn = _workspace(workspace, need)
-    _ok(lib.bkv_compress(ctypes.byref(shape), kp, vp, qp, q_len, window, bp, nbp, nb_max, budget, sp, ip, np_,
-                         ko, vo, wp, wn, _stream(stream)), "bkv_compress")
+    args = (ctypes.byref(shape), kp, vp, qp, q_len, window, bp, nbp, nb_max, budget, sp, ip, np_, ko, vo, wp, wn)
+    return Call(lib.bkv_compress, args, "bkv_compress",
+                (shape, s.seq_len, k, v, q, beacons, n_beacons, scores, idx, n_kept, k_out, v_out, workspace))
+
+
+def compress(s: CacheShape, k, v, q, q_len: int, window: int, beacons, n_beacons, nb_max: int, budget: int,
+             scores, idx, n_kept, k_out, v_out, workspace: Optional[torch.Tensor], stream=None) -> None:
+    """One compression event over every layer: score, select, compact (bkv_compress)."""
+    prepare_compress(s, k, v, q, q_len, window, beacons, n_beacons, nb_max, budget, scores, idx, n_kept, k_out,
+                     v_out, workspace)(stream)

@@ -55,21 +55,32 @@ class CompressionEvent:
         need = bkv.compress_workspace_bytes(self.shape, c.window, c.nb_max, c.budget)
         self.workspace = bkv.alloc_workspace(need, device)
 
-    def update_beacons(self, beacons: List[torch.Tensor], n_beacons: List[torch.Tensor],
-                       q: List[torch.Tensor], stream=None) -> None:
+    def bind(self, k, v, q, beacons, n_beacons) -> "CompressionEvent":
+        """Check the inputs once and prepare every library call of an event over them."""
         c = self.cfg
-        bkv.update_beacons(self.shape, beacons, n_beacons, c.nb_max, q, c.q_len, c.t_new, self.beacons_out,
-                           self.n_beacons_out, stream)
+        sh = self.shape
+        self.calls = {}
+        if c.t_new > 0:
+            self.calls["update_beacons"] = bkv.prepare_update_beacons(sh, beacons, n_beacons, c.nb_max, q, c.q_len,
+                                                                      c.t_new, self.beacons_out, self.n_beacons_out)
+            beacons, n_beacons = self.beacons_out, self.n_beacons_out
+        self.calls["compress"] = bkv.prepare_compress(sh, k, v, q, c.q_len, c.window, beacons, n_beacons, c.nb_max,
+                                                      c.budget, self.scores, self.idx, self.n_kept, self.k_out,
+                                                      self.v_out, self.workspace)
+        # the three stages of compress, separately (for per-stage timing)
+        self.calls["score"] = bkv.prepare_score(sh, k, q, c.q_len, c.window, beacons, n_beacons, c.nb_max,
+                                                self.scores, self.workspace)
+        self.calls["select"] = bkv.prepare_select_topk(sh, self.scores, c.budget, c.window, self.idx, self.n_kept)
+        self.calls["compact"] = bkv.prepare_compact(sh, k, v, self.idx, self.n_kept, c.budget, self.k_out,
+                                                    self.v_out)
+        return self
 
-    def compress(self, k, v, q, beacons, n_beacons, stream=None) -> None:
-        c = self.cfg
-        bkv.compress(self.shape, k, v, q, c.q_len, c.window, beacons, n_beacons, c.nb_max, c.budget, self.scores,
-                     self.idx, self.n_kept, self.k_out, self.v_out, self.workspace, stream)
+    def step(self, stream=None) -> None:
+        """One event over the bound inputs: beacon update (if configured), then compress."""
+        if "update_beacons" in self.calls:
+            self.calls["update_beacons"](stream)
+        self.calls["compress"](stream)
 
     def run(self, k, v, q, beacons, n_beacons, stream=None) -> None:
-        """Beacon update (if configured), then score + select + compact with the refreshed beacons."""
-        if self.cfg.t_new > 0:
-            self.update_beacons(beacons, n_beacons, q, stream)
-            self.compress(k, v, q, self.beacons_out, self.n_beacons_out, stream)
-        else:
-            self.compress(k, v, q, beacons, n_beacons, stream)
+        """Bind the inputs and run one event."""
+        self.bind(k, v, q, beacons, n_beacons).step(stream)

@@ -35,7 +35,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="qwen7b_16k")
-    p.add_argument("--cpu-units", type=int, default=32, help="units in the CPU-oracle sample (0: skip)")
+    p.add_argument("--cpu-units", type=int, default=-1,
+                   help="units in the CPU-oracle sample (0: skip; -1: every unit if at most 160, else 64)")
     p.add_argument("--quiet", action="store_true")
     return p.parse_args()
 
@@ -57,7 +58,7 @@ def alg_bytes(w, lens):
         compact += u * (4 * N * D * 2 + N * 4)
         if w.runs_fps:
             fps += u * ((w.nb_init + G * w.t_new) * D * 2 + w.nb_max * D * 2)
-    return {"score": score, "select": select, "compact": compact, "fps": fps}
+    return {"score": score, "select": select, "compact": compact, "update_beacons": fps}
 
 
 def score_flops(w, lens):
@@ -72,9 +73,14 @@ def cpu_baseline(w, n_units):
     from synth import unit_inputs, bf16_bits, seq_lengths
     from oracle import bkv_oracle as O
     rng = np.random.default_rng(1)
-    lens = seq_lengths(w)
-    units = [(int(rng.integers(w.n_layers)), int(rng.integers(w.batch)), int(rng.integers(w.n_kv_heads)))
-             for _ in range(n_units)]
+    if n_units < 0:
+        n_units = w.units if w.units <= 160 else 64
+    if n_units >= w.units:
+        units = [(l, b, h) for l in range(w.n_layers) for b in range(w.batch) for h in range(w.n_kv_heads)]
+        n_units = len(units)
+    else:
+        units = [(int(rng.integers(w.n_layers)), int(rng.integers(w.batch)), int(rng.integers(w.n_kv_heads)))
+                 for _ in range(n_units)]
     t_total = 0.0
     keys_total = 0
     for (l, b, h) in units:
@@ -93,7 +99,7 @@ def cpu_baseline(w, n_units):
     info = threadpoolctl.threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info] or [1])
     return {"value": tokens_per_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n_units} random (layer, sequence, KV head) units of {w.name}, "
+            "sample": f"{n_units} (layer, sequence, KV head) units of {w.name}, "
                       f"{keys_total} cached rows, {t_total:.1f} s of float64 NumPy "
                       f"(beacon update, scores, top-K, compaction); scaled by layers x KV heads"}
 
@@ -131,8 +137,9 @@ def main():
     stream = torch.cuda.current_stream()
     k, v, q, bc, nb = inp["k"], inp["v"], inp["q"], inp["beacons"], inp["n_beacons"]
 
+    ev.bind(k, v, q, bc, nb)
     for _ in range(args.warmup):
-        ev.run(k, v, q, bc, nb)
+        ev.step()
     torch.cuda.synchronize()
 
     # whole steps
@@ -140,32 +147,26 @@ def main():
     torch.cuda.synchronize()
     e0.record(stream)
     for _ in range(args.steps):
-        ev.run(k, v, q, bc, nb)
+        ev.step()
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
     log(f"[bench] {args.steps} steps, {ms:.3f} ms/step")
 
-    # per-call durations, same stream, same inputs (separate timed loop)
-    scores_bc = ev.beacons_out if w.runs_fps else bc
-    scores_nb = ev.n_beacons_out if w.runs_fps else nb
-    calls = {}
-    if w.runs_fps:
-        calls["fps"] = lambda: ev.update_beacons(bc, nb, q)
-    calls["score"] = lambda: bkv.score(ev.shape, k, q, w.q_len, w.window, scores_bc, scores_nb, w.nb_max, ev.scores,
-                                       ev.workspace)
-    calls["select"] = lambda: bkv.select_topk(ev.shape, ev.scores, w.budget, w.window, ev.idx, ev.n_kept)
-    calls["compact"] = lambda: bkv.compact(ev.shape, k, v, ev.idx, ev.n_kept, w.budget, ev.k_out, ev.v_out)
-    per = {name: 0.0 for name in calls}
-    for _ in range(args.steps):
-        for name, fn in calls.items():
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            fn()
-            b.record(stream)
-            b.synchronize()
-            per[name] += a.elapsed_time(b)
-    per = {n: t / args.steps for n, t in per.items()}
+    # Per-call durations on the same stream: one full event first keeps the GPU busy while
+    # the host enqueues the timed calls, so the events bracket GPU time only.
+    names = (["update_beacons"] if w.runs_fps else []) + ["score", "select", "compact"]
+    per = {}
+    for name in names:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev.step()
+        a.record(stream)
+        for _ in range(args.steps):
+            ev.calls[name]()
+        b.record(stream)
+        torch.cuda.synchronize()
+        per[name] = a.elapsed_time(b) / args.steps
     log("[bench] per call ms: " + ", ".join(f"{n} {t:.3f}" for n, t in per.items()))
 
     tokens = float(lens.sum())
@@ -176,7 +177,7 @@ def main():
     roof = {"kernel": {"score": "score_pass1 + score_merge + score_pass2 (bkv_score)",
                        "select": "select_topk_kernel (bkv_select_topk)",
                        "compact": "compact_kernel (bkv_compact)",
-                       "fps": "fps_kernel (bkv_update_beacons)"}[dom],
+                       "update_beacons": "fps_kernel (bkv_update_beacons)"}[dom],
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
             "ms_per_launch": round(per[dom], 4), "alg_bytes_per_launch": ab[dom]}
@@ -200,8 +201,8 @@ def main():
         "per_call_ms": {n: round(t, 4) for n, t in per.items()},
         "roofline": roof,
     }
-    if args.cpu_units > 0:
-        log(f"[bench] CPU oracle on {args.cpu_units} units ...")
+    if args.cpu_units != 0:
+        log("[bench] CPU oracle on a sample ...")
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_units)
     else:
         out["cpu_baseline"] = None
