@@ -30,14 +30,17 @@ BKV_OK, BKV_EINVAL, BKV_EUNSUPPORTED, BKV_EALIAS, BKV_EWORKSPACE, BKV_EHIP = 0, 
 MAX_OBS = 512
 MAX_POOL = 768
 
-EXPORTS = ["bkv_status_string", "bkv_version", "bkv_update_beacons", "bkv_score_workspace_bytes",
+EXPORTS = ["bkv_status_string", "bkv_version", "bkv_last_error", "bkv_update_beacons", "bkv_score_workspace_bytes",
            "bkv_score", "bkv_select_workspace_bytes", "bkv_select_topk", "bkv_compact",
            "bkv_compress_workspace_bytes", "bkv_compress"]
 
 
 class BkvError(RuntimeError):
     def __init__(self, status: int, what: str):
-        super().__init__(f"{what}: {status_string(status)} ({status})")
+        msg = f"{what}: {status_string(status)} ({status})"
+        if status == BKV_EHIP:
+            msg += " -- " + load().bkv_last_error().decode()
+        super().__init__(msg)
         self.status = status
 
 
@@ -65,6 +68,8 @@ def load() -> ctypes.CDLL:
     lib.bkv_status_string.argtypes = [ctypes.c_int]
     lib.bkv_version.restype = ctypes.c_char_p
     lib.bkv_version.argtypes = []
+    lib.bkv_last_error.restype = ctypes.c_char_p
+    lib.bkv_last_error.argtypes = []
     lib.bkv_update_beacons.restype = ctypes.c_int
     lib.bkv_update_beacons.argtypes = [P(_Shape), arr, arr, i32, arr, i32, i32, arr, arr, vp]
     lib.bkv_score_workspace_bytes.restype = sz

@@ -2,6 +2,7 @@
 // splitting long models into launches of at most kMaxLayers layers, and launches.
 // Nothing here allocates, frees or synchronises.
 #include <math.h>
+#include <stdio.h>
 #include <string.h>
 
 #include <algorithm>
@@ -65,17 +66,17 @@ int obs_pad_of(const bkv_shape* s, int window, int nb_max) {
 int layers_per_launch(const bkv_shape* s) { return std::min(s->n_layers, kMaxLayers); }
 
 struct ScoreWs {
-  size_t part_bytes, lse_bytes, total;
+  size_t part_bytes, total;
 };
 
 ScoreWs score_ws(const bkv_shape* s, int window, int nb_max) {
   ScoreWs w{};
   const size_t units = static_cast<size_t>(layers_per_launch(s)) * s->batch * s->n_kv_heads;
-  const size_t tiles = (static_cast<size_t>(s->capacity) + kScoreTile - 1) / kScoreTile;
-  const size_t obs = static_cast<size_t>(obs_pad_of(s, window, nb_max));
-  w.part_bytes = align_up(units * tiles * obs * sizeof(float));
-  w.lse_bytes = align_up(units * obs * sizeof(float));
-  w.total = 2 * w.part_bytes + w.lse_bytes;
+  const int obs_pad = obs_pad_of(s, window, nb_max);
+  const size_t splits = static_cast<size_t>(score_splits(s->capacity, obs_pad));
+  const size_t obs = static_cast<size_t>(obs_pad);
+  w.part_bytes = align_up(units * splits * obs * sizeof(float));
+  w.total = 2 * w.part_bytes;
   return w;
 }
 
@@ -139,7 +140,15 @@ bkv_status check_compact_args(const bkv_shape* s, const void* const* k, const vo
 
 bkv_status hip_status(hipError_t e) { return e == hipSuccess ? BKV_OK : BKV_EHIP; }
 
+thread_local char g_last_error[256] = "no HIP error recorded";
+
 }  // namespace
+
+hipError_t note_hip_error(hipError_t e, const char* where) {
+  if (e != hipSuccess) snprintf(g_last_error, sizeof(g_last_error), "%s: %s (%d)", where, hipGetErrorString(e), e);
+  return e;
+}
+
 }  // namespace bkv
 
 using namespace bkv;
@@ -158,7 +167,9 @@ const char* bkv_status_string(bkv_status status) {
   return "BKV_?: unknown status";
 }
 
-const char* bkv_version(void) { return "0.1.0"; }
+const char* bkv_version(void) { return "0.2.0"; }
+
+const char* bkv_last_error(void) { return g_last_error; }
 
 size_t bkv_score_workspace_bytes(const bkv_shape* shape, int32_t window, int32_t nb_max) {
   if (check_shape(shape) != BKV_OK || window < 0 || nb_max < 0) return 0;
@@ -177,9 +188,9 @@ bkv_status bkv_score(const bkv_shape* shape, const void* const* k, const void* c
   ScoreArgs a;
   memset(&a, 0, sizeof(a));
   a.seq_len = shape->seq_len;
-  a.part_m = static_cast<float*>(workspace);
-  a.part_z = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.part_bytes);
-  a.lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * ws.part_bytes);
+  char* wsp = static_cast<char*>(workspace);
+  a.part_m = reinterpret_cast<float*>(wsp);
+  a.part_z = reinterpret_cast<float*>(wsp + ws.part_bytes);
   a.batch = shape->batch;
   a.n_q_heads = shape->n_q_heads;
   a.n_kv_heads = shape->n_kv_heads;
@@ -189,7 +200,7 @@ bkv_status bkv_score(const bkv_shape* shape, const void* const* k, const void* c
   a.window = window;
   a.nb_max = nb_max;
   a.obs_pad = obs_pad_of(shape, window, nb_max);
-  a.tiles = (shape->capacity + kScoreTile - 1) / kScoreTile;
+  a.tps = kScoreTilesPerItem;
   a.scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(shape->head_dim)));
   for (int l0 = 0; l0 < shape->n_layers; l0 += kMaxLayers) {
     const int nl = std::min(kMaxLayers, shape->n_layers - l0);

@@ -13,11 +13,10 @@ namespace bkv {
 // One launch covers up to this many layers; the host splits longer models.
 constexpr int kMaxLayers = 48;
 
-// ---- score -------------------------------------------------------------------------------
-// Keys per workgroup tile: 4 waves x 64 keys (two 32-key MFMA fragments per wave).
-constexpr int kScoreWaves = 4;
-constexpr int kKeysPerWave = 64;
-constexpr int kScoreTile = kScoreWaves * kKeysPerWave;
+// ---- score ----------------------------------------------------------------------------------
+// Two grid-stride kernels per chunk of units (see score.hip).  Key tiles are WAVES*64 keys;
+// an item is kScoreTilesPerItem consecutive tiles of one unit.
+constexpr int kScoreTilesPerItem = 4;
 
 struct ScoreArgs {
   const uint16_t* k[kMaxLayers];
@@ -26,16 +25,26 @@ struct ScoreArgs {
   const int32_t* n_beacons[kMaxLayers];
   float* scores[kMaxLayers];
   const int32_t* seq_len;
-  float* part_m;        // [unit][tile][obs_pad] running max (log2 domain)
-  float* part_z;        // [unit][tile][obs_pad] sum of exp2(t - m)
-  float* lse;           // [unit][obs_pad] log2-sum-exp2 per observation row
+  float* part_m;        // [unit][split][obs_pad] running max (log2 domain)
+  float* part_z;        // [unit][split][obs_pad] sum of exp2(t - m)
   int batch, n_q_heads, n_kv_heads, group, capacity;
   int q_len, window, nb_max;
   int obs_pad;          // observation rows per unit rounded up to 32 (launch-wide)
-  int tiles;            // ceil(capacity / kScoreTile)
-  int units;            // units in this launch (layers * batch * n_kv_heads)
+  int unit0;            // first unit of the current chunk (set by the launcher)
+  int units;            // units in the chunk (the whole call on entry to the launcher)
+  int tps;              // tiles per item
+  int splits;           // items per unit (set by the launcher)
   float scale_log2;     // log2(e) / sqrt(head_dim)
 };
+
+// Waves per score workgroup for a given padded observation count, and the split count the
+// launcher will use (the workspace is sized from these).
+int score_waves(int obs_pad);
+inline int score_splits(int capacity, int obs_pad) {
+  const int tile = score_waves(obs_pad) * 64;
+  const int ntiles = (capacity + tile - 1) / tile;
+  return (ntiles + kScoreTilesPerItem - 1) / kScoreTilesPerItem;
+}
 
 // ---- select ------------------------------------------------------------------------------
 constexpr int kSelectThreads = 1024;
@@ -78,5 +87,9 @@ hipError_t launch_compact(const CompactArgs& a, int n_layers, int head_dim, hipS
 hipError_t launch_fps(const FpsArgs& a, int n_layers, int head_dim, int pool_max, hipStream_t s);
 
 inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+// Remember the HIP error behind a BKV_EHIP (per calling thread) together with the name of
+// the call that returned it; returns `e` unchanged.
+hipError_t note_hip_error(hipError_t e, const char* where);
 
 }  // namespace bkv

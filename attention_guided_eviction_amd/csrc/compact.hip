@@ -44,7 +44,7 @@ hipError_t launch_compact(const CompactArgs& a, int n_layers, int head_dim, hipS
     hipLaunchKernelGGL(compact_kernel<128>, dim3(grid), dim3(kThreads), 0, s, a, blocks_per_unit);
   else
     hipLaunchKernelGGL(compact_kernel<64>, dim3(grid), dim3(kThreads), 0, s, a, blocks_per_unit);
-  return hipGetLastError();
+  return note_hip_error(hipGetLastError(), "compact: launch");
 }
 
 }  // namespace bkv

@@ -166,7 +166,7 @@ hipError_t launch_fps(const FpsArgs& a, int n_layers, int head_dim, int pool_max
       hipLaunchKernelGGL((fps_kernel<128, R>), dim3(grid), dim3(kFpsThreads), 0, s, a);  \
     else                                                                                  \
       hipLaunchKernelGGL((fps_kernel<64, R>), dim3(grid), dim3(kFpsThreads), 0, s, a);   \
-    return hipGetLastError();                                                             \
+    return note_hip_error(hipGetLastError(), "fps: launch");                                                             \
   }
   BKV_FPS_CASE(1)
   BKV_FPS_CASE(2)

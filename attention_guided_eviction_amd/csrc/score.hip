@@ -7,16 +7,21 @@
 // where lse_i normalises row i over all valid keys.  Everything runs in the log2
 // domain: t_ij = s_ij * log2(e) and score_j = exp2(max_i(t_ij - lse2_i)).
 //
-// Two passes over K, each one MFMA contraction of a 256-key tile with all observation
-// rows (bf16 inputs, fp32 accumulation):
-//   pass 1  per (unit, tile): row max and sum of exp2 over the tile's keys;
-//   merge   per (unit, row):  lse2 = M + log2(sum_t z_t * exp2(m_t - M));
-//   pass 2  per (unit, tile): recompute the logits, take max_i(t_ij - lse2_i), exp2.
+// Two kernels per chunk of units, each a grid-stride loop over items (unit, split); an
+// item is a run of key tiles of one unit.  No workgroup ever waits for another:
+//   score_stats   logits of the item's tiles against every observation row, per-row
+//                 running max and sum of exp2 -> partial (m, z) per (unit, split, row);
+//   score_finish  merges the unit's partials into lse2 per row (in LDS), recomputes
+//                 the logits and writes exp2(max_i(t_ij - lse2_i)) for its keys.
+// The host walks the units in chunks of at most ~128 MB of keys, stats then finish per
+// chunk, so the second read of a chunk's keys comes from the last-level cache.
 //
 // MFMA mapping (v_mfma_f32_32x32x16_bf16): the A operand is 32 keys x 16 dims, the B
 // operand 16 dims x 32 observation rows, so one lane's 16 accumulators are 16 keys of
-// one observation row.  Row statistics (pass 1) therefore reduce inside a lane, and the
-// per-key max (pass 2) is one cross-lane reduction at the end of the tile.
+// one observation row.  Row statistics reduce inside a lane; the per-key max is one
+// cross-lane reduction per key tile.  Key fragments for the next tile are loaded while
+// the current one is multiplied.
+#include <algorithm>
 #include <mutex>
 
 #include "bkv_internal.h"
@@ -28,11 +33,13 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 constexpr float kNegInf = -__builtin_inff();
+constexpr float kPosInf = __builtin_inff();
 
 struct UnitInfo {
-  int layer, b, h, L, n_obs;
+  int layer, b, h, L, n_obs, nqb, ntiles, nsplits;
 };
 
+template <int WAVES>
 __device__ inline UnitInfo unit_info(const ScoreArgs& a, int u) {
   UnitInfo ui;
   const int per_layer = a.batch * a.n_kv_heads;
@@ -48,19 +55,22 @@ __device__ inline UnitInfo unit_info(const ScoreArgs& a, int u) {
     nb = nb < 0 ? 0 : (nb > a.nb_max ? a.nb_max : nb);
   }
   ui.n_obs = a.group * a.window + nb;
+  ui.nqb = (ui.n_obs + 31) >> 5;
+  ui.ntiles = (ui.L + WAVES * 64 - 1) / (WAVES * 64);
+  ui.nsplits = (ui.ntiles + a.tps - 1) / a.tps;
   return ui;
 }
 
 // Stage the unit's observation rows in LDS (row stride D*2+16 bytes keeps the 16-byte
 // fragment reads of 8 consecutive rows on distinct banks); rows n_obs..nqb*32-1 are zero.
 template <int D>
-__device__ inline void stage_queries(const ScoreArgs& a, const UnitInfo& ui, int nqb, uint8_t* qs) {
+__device__ inline void stage_queries(const ScoreArgs& a, const UnitInfo& ui, uint8_t* qs) {
   constexpr int kRowBytes = D * 2 + 16;
   constexpr int kChunks = D / 8;
   const int gw = a.group * a.window;
   const uint16_t* q = a.q[ui.layer];
   const uint16_t* bc = a.nb_max > 0 ? a.beacons[ui.layer] : nullptr;
-  for (int c = threadIdx.x; c < nqb * 32 * kChunks; c += blockDim.x) {
+  for (int c = threadIdx.x; c < ui.nqb * 32 * kChunks; c += blockDim.x) {
     const int r = c / kChunks;
     const int cc = c - r * kChunks;
     uint4 v = make_uint4(0, 0, 0, 0);
@@ -77,11 +87,16 @@ __device__ inline void stage_queries(const ScoreArgs& a, const UnitInfo& ui, int
   }
 }
 
-// Load two 32-key A fragments.  Lane l holds key (l & 31) of each fragment and, for
-// k-step s, dims 16*s + 8*(l >> 5) .. +7.  Keys past the valid length read row L-1
-// (always in bounds) and are masked by the caller.
+// Two 32-key A fragments.  Lane l holds key (l & 31) of each fragment and, for k-step
+// s, dims 16*s + 8*(l >> 5) .. +7.  Keys past the valid length read row L-1 (always in
+// bounds) and are masked by the caller.
 template <int D>
-__device__ inline void load_key_fragments(const uint16_t* kp, int kbase, int L, bf16x8 (&kf)[2][D / 16]) {
+struct KeyFrag {
+  bf16x8 v[2][D / 16];
+};
+
+template <int D>
+__device__ inline void load_keys(const uint16_t* kp, int kbase, int L, KeyFrag<D>& kf) {
   const int lane = threadIdx.x & 63;
   const int row = lane & 31;
   const int half = lane >> 5;
@@ -91,12 +106,12 @@ __device__ inline void load_key_fragments(const uint16_t* kp, int kbase, int L, 
     key = key < L ? key : L - 1;
     const uint16_t* src = kp + static_cast<size_t>(key) * D + half * 8;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) kf[f][s] = *reinterpret_cast<const bf16x8*>(src + s * 16);
+    for (int s = 0; s < D / 16; ++s) kf.v[f][s] = *reinterpret_cast<const bf16x8*>(src + s * 16);
   }
 }
 
 template <int D>
-__device__ inline void mfma_block(const bf16x8 (&kf)[2][D / 16], const uint8_t* qs, int qb, f32x16 (&acc)[2]) {
+__device__ inline void mfma_block(const KeyFrag<D>& kf, const uint8_t* qs, int qb, f32x16 (&acc)[2]) {
   constexpr int kRowBytes = D * 2 + 16;
   const int lane = threadIdx.x & 63;
   const uint8_t* qrow = qs + (qb * 32 + (lane & 31)) * kRowBytes + (lane >> 5) * 16;
@@ -107,7 +122,7 @@ __device__ inline void mfma_block(const bf16x8 (&kf)[2][D / 16], const uint8_t* 
   for (int f = 0; f < 2; ++f) {
     f32x16 c = {};
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[f][s], qf[s], c, 0, 0, 0);
+    for (int s = 0; s < D / 16; ++s) c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.v[f][s], qf[s], c, 0, 0, 0);
     acc[f] = c;
   }
 }
@@ -125,171 +140,235 @@ __device__ inline void merge_stats(float& m, float& z, float m2, float z2) {
   m = M;
 }
 
-template <int D>
-__global__ __launch_bounds__(kScoreWaves * 64) void score_pass1(const ScoreArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int u = blockIdx.x / a.tiles;
-  const int tile = blockIdx.x - u * a.tiles;
-  const UnitInfo ui = unit_info(a, u);
-  const int tile0 = tile * kScoreTile;
-  if (tile0 >= ui.L) return;
-  const int nqb = (ui.n_obs + 31) >> 5;
-  uint8_t* qs = smem;
-  float* st_m = reinterpret_cast<float*>(smem + a.obs_pad * (D * 2 + 16));
-  float* st_z = st_m + kScoreWaves * a.obs_pad;
-  stage_queries<D>(a, ui, nqb, qs);
+template <int D, int WAVES>
+struct Smem {
+  static constexpr int kRowBytes = D * 2 + 16;
+  uint8_t* qs;
+  float* st_m;   // [WAVES][obs_pad] (pass 1)
+  float* st_z;   // [WAVES][obs_pad] (pass 1)
+  float* lse_s;  // [obs_pad]        (pass 2; aliases st_m)
+  __device__ Smem(uint8_t* base, int obs_pad) {
+    qs = base;
+    st_m = reinterpret_cast<float*>(base + obs_pad * kRowBytes);
+    st_z = st_m + WAVES * obs_pad;
+    lse_s = st_m;
+  }
+};
 
+template <int D, int WAVES>
+__device__ void pass1_item(const ScoreArgs& a, int u, int split, const UnitInfo& ui, uint8_t* smem) {
+  Smem<D, WAVES> sm(smem, a.obs_pad);
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int kbase = tile0 + wave * kKeysPerWave;
+  stage_queries<D>(a, ui, sm.qs);
+  for (int i = threadIdx.x; i < WAVES * a.obs_pad; i += blockDim.x) {
+    sm.st_m[i] = kNegInf;
+    sm.st_z[i] = 0.f;
+  }
+  const int t0 = split * a.tps;
+  const int t1 = min(t0 + a.tps, ui.ntiles);
   const uint16_t* kp = a.k[ui.layer] + (static_cast<size_t>(ui.b) * a.n_kv_heads + ui.h) * a.capacity * D;
-  bf16x8 kf[2][D / 16];
-  load_key_fragments<D>(kp, kbase, ui.L, kf);
+  KeyFrag<D> cur, nxt;
+  load_keys<D>(kp, t0 * WAVES * 64 + wave * 64, ui.L, cur);
   __syncthreads();
-
-  for (int qb = 0; qb < nqb; ++qb) {
-    f32x16 acc[2];
-    mfma_block<D>(kf, qs, qb, acc);
-    float m = kNegInf;
+  float* my_m = sm.st_m + wave * a.obs_pad;
+  float* my_z = sm.st_z + wave * a.obs_pad;
+  for (int t = t0; t < t1; ++t) {
+    const int kbase = t * WAVES * 64 + wave * 64;
+    if (t + 1 < t1) load_keys<D>(kp, kbase + WAVES * 64, ui.L, nxt);
+    const bool full = kbase + 64 <= ui.L;
+    if (kbase < ui.L) {
+      for (int qb = 0; qb < ui.nqb; ++qb) {
+        f32x16 acc[2];
+        mfma_block<D>(cur, sm.qs, qb, acc);
+        float mx = kNegInf;
+        if (full) {
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
+          for (int f = 0; f < 2; ++f)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float t = kbase + acc_key(f, r, lane) < ui.L ? acc[f][r] * a.scale_log2 : kNegInf;
-        acc[f][r] = t;
-        m = fmaxf(m, t);
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[f][r]);
+        } else {
+#pragma unroll
+          for (int f = 0; f < 2; ++f)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const float x = kbase + acc_key(f, r, lane) < ui.L ? acc[f][r] : kNegInf;
+              acc[f][r] = x;
+              mx = fmaxf(mx, x);
+            }
+        }
+        float m = mx * a.scale_log2;   // scale > 0 commutes with max
+        float z = 0.f;
+        if (mx != kNegInf) {
+          const float neg = -m;
+#pragma unroll
+          for (int f = 0; f < 2; ++f)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) z += __builtin_amdgcn_exp2f(fmaf(acc[f][r], a.scale_log2, neg));
+        } else {
+          m = kNegInf;
+        }
+        merge_stats(m, z, __shfl_xor(m, 32), __shfl_xor(z, 32));
+        if (lane < 32) {
+          const int row = qb * 32 + lane;
+          float pm = my_m[row], pz = my_z[row];
+          merge_stats(pm, pz, m, z);
+          my_m[row] = pm;
+          my_z[row] = pz;
+        }
       }
-    float z = 0.f;
-    if (m != kNegInf) {
-#pragma unroll
-      for (int f = 0; f < 2; ++f)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) z += __builtin_amdgcn_exp2f(acc[f][r] - m);
     }
-    merge_stats(m, z, __shfl_xor(m, 32), __shfl_xor(z, 32));
-    if (lane < 32) {
-      st_m[wave * a.obs_pad + qb * 32 + lane] = m;
-      st_z[wave * a.obs_pad + qb * 32 + lane] = z;
-    }
+    if (t + 1 < t1) cur = nxt;
   }
   __syncthreads();
-  const size_t base = (static_cast<size_t>(u) * a.tiles + tile) * a.obs_pad;
-  for (int i = threadIdx.x; i < nqb * 32; i += blockDim.x) {
-    float m = st_m[i], z = st_z[i];
+  const size_t base = (static_cast<size_t>(u) * a.splits + split) * a.obs_pad;
+  for (int i = threadIdx.x; i < ui.nqb * 32; i += blockDim.x) {
+    float m = sm.st_m[i], z = sm.st_z[i];
 #pragma unroll
-    for (int w = 1; w < kScoreWaves; ++w) merge_stats(m, z, st_m[w * a.obs_pad + i], st_z[w * a.obs_pad + i]);
+    for (int w = 1; w < WAVES; ++w) merge_stats(m, z, sm.st_m[w * a.obs_pad + i], sm.st_z[w * a.obs_pad + i]);
     a.part_m[base + i] = m;
     a.part_z[base + i] = z;
   }
+  __syncthreads();   // LDS is restaged by the next item
 }
 
-__global__ __launch_bounds__(256) void score_merge(const ScoreArgs a) {
-  const int u = blockIdx.x;
-  const UnitInfo ui = unit_info(a, u);
-  const int ntiles = (ui.L + kScoreTile - 1) / kScoreTile;
-  for (int i = threadIdx.x; i < a.obs_pad; i += blockDim.x) {
-    float M = kNegInf;
-    const size_t base = static_cast<size_t>(u) * a.tiles * a.obs_pad + i;
-    for (int t = 0; t < ntiles; ++t) M = fmaxf(M, a.part_m[base + static_cast<size_t>(t) * a.obs_pad]);
-    float Z = 0.f;
-    if (M != kNegInf)
-      for (int t = 0; t < ntiles; ++t) {
-        const size_t o = base + static_cast<size_t>(t) * a.obs_pad;
-        Z += a.part_z[o] * __builtin_amdgcn_exp2f(a.part_m[o] - M);
-      }
-    // Rows past n_obs (padding) and units without keys get +inf: they never win a max.
-    a.lse[static_cast<size_t>(u) * a.obs_pad + i] =
-        (i < ui.n_obs && Z > 0.f) ? M + log2f(Z) : __builtin_inff();
-  }
-}
-
-template <int D>
-__global__ __launch_bounds__(kScoreWaves * 64) void score_pass2(const ScoreArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int u = blockIdx.x / a.tiles;
-  const int tile = blockIdx.x - u * a.tiles;
-  const UnitInfo ui = unit_info(a, u);
-  const int tile0 = tile * kScoreTile;
-  if (tile0 >= ui.L) return;
-  const int nqb = (ui.n_obs + 31) >> 5;
-  uint8_t* qs = smem;
-  float* lse_s = reinterpret_cast<float*>(smem + a.obs_pad * (D * 2 + 16));
-  stage_queries<D>(a, ui, nqb, qs);
-  for (int i = threadIdx.x; i < nqb * 32; i += blockDim.x) lse_s[i] = a.lse[static_cast<size_t>(u) * a.obs_pad + i];
-
+template <int D, int WAVES>
+__device__ void pass2_item(const ScoreArgs& a, int u, int split, const UnitInfo& ui, uint8_t* smem) {
+  Smem<D, WAVES> sm(smem, a.obs_pad);
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int kbase = tile0 + wave * kKeysPerWave;
+  const int t0 = split * a.tps;
+  const int t1 = min(t0 + a.tps, ui.ntiles);
   const uint16_t* kp = a.k[ui.layer] + (static_cast<size_t>(ui.b) * a.n_kv_heads + ui.h) * a.capacity * D;
-  bf16x8 kf[2][D / 16];
-  load_key_fragments<D>(kp, kbase, ui.L, kf);
-  __syncthreads();
-
-  float v[32];
-#pragma unroll
-  for (int i = 0; i < 32; ++i) v[i] = kNegInf;
-  for (int qb = 0; qb < nqb; ++qb) {
-    f32x16 acc[2];
-    mfma_block<D>(kf, qs, qb, acc);
-    const float neg_lse = -lse_s[qb * 32 + (lane & 31)];
-#pragma unroll
-    for (int f = 0; f < 2; ++f)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) v[f * 16 + r] = fmaxf(v[f * 16 + r], fmaf(acc[f][r], a.scale_log2, neg_lse));
-  }
-  // Max over the 32 observation rows held by lanes l ^ {1,2,4,8,16}: each exchange step
-  // halves the values a lane keeps, so lane l ends with value index (l & 31).
-#pragma unroll
-  for (int step = 16, n = 16; step >= 1; step >>= 1, n >>= 1) {
-    const bool upper = (lane & step) != 0;
-#pragma unroll
-    for (int i = 0; i < n; ++i) {
-      const float send = upper ? v[i] : v[i + n];
-      const float keep = upper ? v[i + n] : v[i];
-      v[i] = fmaxf(keep, __shfl_xor(send, step));
+  float* sp = a.scores[ui.layer] + (static_cast<size_t>(ui.b) * a.n_kv_heads + ui.h) * a.capacity;
+  KeyFrag<D> cur, nxt;
+  load_keys<D>(kp, t0 * WAVES * 64 + wave * 64, ui.L, cur);
+  stage_queries<D>(a, ui, sm.qs);
+  // log2-sum-exp2 of every observation row from the unit's stats partials.
+  for (int i = threadIdx.x; i < ui.nqb * 32; i += blockDim.x) {
+    float M = kNegInf, Z = 0.f;
+    for (int sp_ = 0; sp_ < ui.nsplits; ++sp_) {
+      const size_t o = (static_cast<size_t>(u) * a.splits + sp_) * a.obs_pad + i;
+      merge_stats(M, Z, a.part_m[o], a.part_z[o]);
     }
+    // Padding rows get +inf: they never win the max.
+    sm.lse_s[i] = (i < ui.n_obs && Z > 0.f) ? M + log2f(Z) : kPosInf;
   }
-  const int vi = lane & 31;
-  const int key = kbase + acc_key(vi >> 4, vi & 15, lane);
-  if (key < ui.L) {
-    float* sp = a.scores[ui.layer] + (static_cast<size_t>(ui.b) * a.n_kv_heads + ui.h) * a.capacity;
-    sp[key] = ui.n_obs > 0 ? exp2f(v[0]) : 0.f;
+  __syncthreads();
+  for (int t = t0; t < t1; ++t) {
+    const int kbase = t * WAVES * 64 + wave * 64;
+    if (t + 1 < t1) load_keys<D>(kp, kbase + WAVES * 64, ui.L, nxt);
+    if (kbase < ui.L) {
+      float v[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) v[i] = kNegInf;
+      for (int qb = 0; qb < ui.nqb; ++qb) {
+        f32x16 acc[2];
+        mfma_block<D>(cur, sm.qs, qb, acc);
+        const float neg_lse = -sm.lse_s[qb * 32 + (lane & 31)];
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) v[f * 16 + r] = fmaxf(v[f * 16 + r], fmaf(acc[f][r], a.scale_log2, neg_lse));
+      }
+      // Max over the 32 observation rows held by lanes l ^ {16,8,4,2,1}: each exchange
+      // halves the values a lane keeps, so lane l ends with value index (l & 31).
+#pragma unroll
+      for (int step = 16; step >= 1; step >>= 1) {
+        const bool upper = (lane & step) != 0;
+#pragma unroll
+        for (int i = 0; i < step; ++i) {
+          const float send = upper ? v[i] : v[i + step];
+          const float keep = upper ? v[i + step] : v[i];
+          v[i] = fmaxf(keep, __shfl_xor(send, step));
+        }
+      }
+      const int vi = lane & 31;
+      const int key = kbase + acc_key(vi >> 4, vi & 15, lane);
+      if (key < ui.L) sp[key] = ui.n_obs > 0 ? exp2f(v[0]) : 0.f;
+    }
+    if (t + 1 < t1) cur = nxt;
+  }
+  __syncthreads();   // LDS is restaged by the next item
+}
+
+template <int D, int WAVES, bool FINISH>
+__global__ __launch_bounds__(WAVES * 64) void score_kernel(const ScoreArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int n_items = a.units * a.splits;
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int u = a.unit0 + item / a.splits;
+    const int split = item - (item / a.splits) * a.splits;
+    const UnitInfo ui = unit_info<WAVES>(a, u);
+    if (split >= ui.nsplits) continue;   // no keys in this split (uniform across the block)
+    if (FINISH)
+      pass2_item<D, WAVES>(a, u, split, ui, smem);
+    else
+      pass1_item<D, WAVES>(a, u, split, ui, smem);
   }
 }
 
-template <int D>
-size_t score_lds_bytes(int obs_pad) {
-  return static_cast<size_t>(obs_pad) * (D * 2 + 16) + 2 * kScoreWaves * obs_pad * sizeof(float);
+template <int D, int WAVES>
+size_t lds_bytes(int obs_pad) {
+  return static_cast<size_t>(obs_pad) * (D * 2 + 16) + 2 * WAVES * obs_pad * sizeof(float);
 }
 
-template <int D>
-hipError_t launch_score_d(const ScoreArgs& a, hipStream_t s) {
-  const size_t lds = score_lds_bytes<D>(a.obs_pad);
+template <int D, int WAVES>
+hipError_t launch_d(ScoreArgs a, hipStream_t s) {
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, [] {
-    attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&score_pass1<D>),
+    attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&score_kernel<D, WAVES, false>),
                                    hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (attr_err == hipSuccess)
-      attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&score_pass2<D>),
+      attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&score_kernel<D, WAVES, true>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   });
-  if (attr_err != hipSuccess) return attr_err;
-  const unsigned grid = static_cast<unsigned>(a.units) * a.tiles;
-  hipLaunchKernelGGL(score_pass1<D>, dim3(grid), dim3(kScoreWaves * 64), lds, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(score_merge, dim3(a.units), dim3(256), 0, s, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(score_pass2<D>, dim3(grid), dim3(kScoreWaves * 64), lds, s, a);
-  return hipGetLastError();
+  if (attr_err != hipSuccess) return note_hip_error(attr_err, "score: hipFuncSetAttribute");
+  const size_t lds = lds_bytes<D, WAVES>(a.obs_pad);
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return note_hip_error(e, "score: hipGetDevice");
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return note_hip_error(e, "score: hipDeviceGetAttribute");
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, score_kernel<D, WAVES, true>, WAVES * 64, lds);
+  if (e != hipSuccess) return note_hip_error(e, "score: hipOccupancyMaxActiveBlocksPerMultiprocessor");
+  const int resident = std::max(1, per_cu) * cus;
+  a.tps = kScoreTilesPerItem;
+  a.splits = score_splits(a.capacity, a.obs_pad);
+  // Chunks of whole units with at most ~128 MB of keys (half the last-level cache), so
+  // score_finish re-reads keys that score_stats has just brought in.
+  const long long unit_bytes = static_cast<long long>(a.capacity) * D * 2;
+  const int per_chunk = static_cast<int>(std::max(1ll, (128ll << 20) / std::max(1ll, unit_bytes)));
+  const int total_units = a.units;
+  for (int u0 = 0; u0 < total_units; u0 += per_chunk) {
+    a.unit0 = u0;
+    a.units = std::min(per_chunk, total_units - u0);
+    const int grid = std::min(resident, a.units * a.splits);
+    hipLaunchKernelGGL((score_kernel<D, WAVES, false>), dim3(grid), dim3(WAVES * 64), lds, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return note_hip_error(e, "score: launch score_stats");
+    hipLaunchKernelGGL((score_kernel<D, WAVES, true>), dim3(grid), dim3(WAVES * 64), lds, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return note_hip_error(e, "score: launch score_finish");
+  }
+  return hipSuccess;
 }
 
 }  // namespace
 
+int score_waves(int obs_pad) { return obs_pad <= 384 ? 8 : 4; }
+
+size_t score_lds_bytes(int head_dim, int obs_pad) {
+  const int w = score_waves(obs_pad);
+  if (head_dim == 128) return w == 8 ? lds_bytes<128, 8>(obs_pad) : lds_bytes<128, 4>(obs_pad);
+  return w == 8 ? lds_bytes<64, 8>(obs_pad) : lds_bytes<64, 4>(obs_pad);
+}
+
 hipError_t launch_score(const ScoreArgs& a, int /*n_layers*/, int head_dim, hipStream_t s) {
-  return head_dim == 128 ? launch_score_d<128>(a, s) : launch_score_d<64>(a, s);
+  const int w = score_waves(a.obs_pad);
+  if (head_dim == 128) return w == 8 ? launch_d<128, 8>(a, s) : launch_d<128, 4>(a, s);
+  return w == 8 ? launch_d<64, 8>(a, s) : launch_d<64, 4>(a, s);
 }
 
 }  // namespace bkv

@@ -139,7 +139,7 @@ hipError_t launch_select(const SelectArgs& a, int n_layers, hipStream_t s) {
 #define BKV_SELECT_CASE(E)                                                                        \
   if (ept <= E) {                                                                                 \
     hipLaunchKernelGGL(select_topk_kernel<E>, dim3(grid), dim3(kSelectThreads), 0, s, a);      \
-    return hipGetLastError();                                                                     \
+    return note_hip_error(hipGetLastError(), "select: launch");                                                                     \
   }
   BKV_SELECT_CASE(1)
   BKV_SELECT_CASE(2)

@@ -90,8 +90,12 @@ typedef struct bkv_shape {
 /* Human-readable name of a status code (static string, never NULL). */
 const char* bkv_status_string(bkv_status status);
 
-/* Library version, e.g. "0.1.0" (static string). */
+/* Library version, e.g. "0.2.0" (static string). */
 const char* bkv_version(void);
+
+/* Which HIP call failed, and how, for this thread's most recent BKV_EHIP (a thread-local
+ * string valid until the thread's next failing call; "no HIP error recorded" if none). */
+const char* bkv_last_error(void);
 
 /* ------------------------------------------------------------------------------------
  * Continual farthest-point sampling of beacon queries.
