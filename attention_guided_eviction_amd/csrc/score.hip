@@ -63,27 +63,43 @@ __device__ inline UnitInfo unit_info(const ScoreArgs& a, int u) {
 
 // Stage the unit's observation rows in LDS (row stride D*2+16 bytes keeps the 16-byte
 // fragment reads of 8 consecutive rows on distinct banks); rows n_obs..nqb*32-1 are zero.
+// Each thread issues its loads in batches of 8 before waiting, so the staging costs about
+// one memory latency per batch rather than one per row chunk.
 template <int D>
 __device__ inline void stage_queries(const ScoreArgs& a, const UnitInfo& ui, uint8_t* qs) {
   constexpr int kRowBytes = D * 2 + 16;
   constexpr int kChunks = D / 8;
+  constexpr int kBatch = 8;
   const int gw = a.group * a.window;
   const uint16_t* q = a.q[ui.layer];
   const uint16_t* bc = a.nb_max > 0 ? a.beacons[ui.layer] : nullptr;
-  for (int c = threadIdx.x; c < ui.nqb * 32 * kChunks; c += blockDim.x) {
-    const int r = c / kChunks;
-    const int cc = c - r * kChunks;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (r < gw) {
-      const int hq = ui.h * a.group + r / a.window;
-      const int t = a.q_len - a.window + r % a.window;
-      v = *reinterpret_cast<const uint4*>(
-          q + ((static_cast<size_t>(ui.b) * a.n_q_heads + hq) * a.q_len + t) * D + cc * 8);
-    } else if (r < ui.n_obs) {
-      v = *reinterpret_cast<const uint4*>(
-          bc + ((static_cast<size_t>(ui.b) * a.n_kv_heads + ui.h) * a.nb_max + (r - gw)) * D + cc * 8);
+  const int total = ui.nqb * 32 * kChunks;
+  for (int c0 = threadIdx.x; c0 < total; c0 += kBatch * blockDim.x) {
+    uint4 v[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int c = c0 + j * blockDim.x;
+      const int r = c / kChunks;
+      const int cc = c - r * kChunks;
+      v[j] = make_uint4(0, 0, 0, 0);
+      if (c < total) {
+        if (r < gw) {
+          const int hq = ui.h * a.group + r / a.window;
+          const int t = a.q_len - a.window + r % a.window;
+          v[j] = *reinterpret_cast<const uint4*>(
+              q + ((static_cast<size_t>(ui.b) * a.n_q_heads + hq) * a.q_len + t) * D + cc * 8);
+        } else if (r < ui.n_obs) {
+          v[j] = *reinterpret_cast<const uint4*>(
+              bc + ((static_cast<size_t>(ui.b) * a.n_kv_heads + ui.h) * a.nb_max + (r - gw)) * D + cc * 8);
+        }
+      }
     }
-    *reinterpret_cast<uint4*>(qs + r * kRowBytes + cc * 16) = v;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int c = c0 + j * blockDim.x;
+      const int r = c / kChunks;
+      if (c < total) *reinterpret_cast<uint4*>(qs + r * kRowBytes + (c - r * kChunks) * 16) = v[j];
+    }
   }
 }
 
@@ -111,20 +127,24 @@ __device__ inline void load_keys(const uint16_t* kp, int kbase, int L, KeyFrag<D
 }
 
 template <int D>
-__device__ inline void mfma_block(const KeyFrag<D>& kf, const uint8_t* qs, int qb, f32x16 (&acc)[2]) {
+__device__ inline void load_qfrag(const uint8_t* qs, int qb, bf16x8 (&qf)[D / 16]) {
   constexpr int kRowBytes = D * 2 + 16;
   const int lane = threadIdx.x & 63;
   const uint8_t* qrow = qs + (qb * 32 + (lane & 31)) * kRowBytes + (lane >> 5) * 16;
-  bf16x8 qf[D / 16];
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + s * 32);
+}
+
+template <int D>
+__device__ inline void mfma_frags(const KeyFrag<D>& kf, const bf16x8 (&qf)[D / 16], f32x16 (&acc)[2]) {
+  f32x16 c0 = {}, c1 = {};
 #pragma unroll
-  for (int f = 0; f < 2; ++f) {
-    f32x16 c = {};
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.v[f][s], qf[s], c, 0, 0, 0);
-    acc[f] = c;
+  for (int s = 0; s < D / 16; ++s) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.v[0][s], qf[s], c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.v[1][s], qf[s], c1, 0, 0, 0);
   }
+  acc[0] = c0;
+  acc[1] = c1;
 }
 
 // Key offset (within the wave's 64 keys) of accumulator r of fragment f in lane l.
@@ -144,16 +164,46 @@ template <int D, int WAVES>
 struct Smem {
   static constexpr int kRowBytes = D * 2 + 16;
   uint8_t* qs;
-  float* st_m;   // [WAVES][obs_pad] (pass 1)
-  float* st_z;   // [WAVES][obs_pad] (pass 1)
+  float* st_m;   // [WAVES][2][obs_pad] (pass 1): per wave and lane half
+  float* st_z;   // [WAVES][2][obs_pad] (pass 1)
   float* lse_s;  // [obs_pad]        (pass 2; aliases st_m)
   __device__ Smem(uint8_t* base, int obs_pad) {
     qs = base;
     st_m = reinterpret_cast<float*>(base + obs_pad * kRowBytes);
-    st_z = st_m + WAVES * obs_pad;
+    st_z = st_m + 2 * WAVES * obs_pad;
     lse_s = st_m;
   }
 };
+
+// Keys at or past L (only in a unit's last tile) get -inf logits.
+__device__ inline void mask_tail(f32x16 (&acc)[2], int kbase, int L, int lane) {
+#pragma unroll
+  for (int f = 0; f < 2; ++f)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (kbase + acc_key(f, r, lane) >= L) acc[f][r] = kNegInf;
+}
+
+// Exact (max, sum) update of one lane's 32 logits of one row: the block max is taken and
+// the running sum rescaled.  Used for a row's first block and when the cheap update below
+// reports a possible overflow.
+__device__ inline void row_update_exact(const f32x16 (&acc)[2], float c, float& m, float& z) {
+  float mx = kNegInf;
+#pragma unroll
+  for (int f = 0; f < 2; ++f)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[f][r]);
+  if (mx == kNegInf) return;   // every key of this lane masked
+  const float mt = fmaxf(mx * c, m);
+  float zt = 0.f;
+  const float neg = -mt;
+#pragma unroll
+  for (int f = 0; f < 2; ++f)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) zt += __builtin_amdgcn_exp2f(fmaf(acc[f][r], c, neg));
+  z = (m == kNegInf ? 0.f : z * __builtin_amdgcn_exp2f(m - mt)) + zt;
+  m = mt;
+}
 
 template <int D, int WAVES>
 __device__ void pass1_item(const ScoreArgs& a, int u, int split, const UnitInfo& ui, uint8_t* smem) {
@@ -161,71 +211,78 @@ __device__ void pass1_item(const ScoreArgs& a, int u, int split, const UnitInfo&
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   stage_queries<D>(a, ui, sm.qs);
-  for (int i = threadIdx.x; i < WAVES * a.obs_pad; i += blockDim.x) {
+  for (int i = threadIdx.x; i < 2 * WAVES * a.obs_pad; i += blockDim.x) {
     sm.st_m[i] = kNegInf;
     sm.st_z[i] = 0.f;
   }
   const int t0 = split * a.tps;
   const int t1 = min(t0 + a.tps, ui.ntiles);
   const uint16_t* kp = a.k[ui.layer] + (static_cast<size_t>(ui.b) * a.n_kv_heads + ui.h) * a.capacity * D;
-  KeyFrag<D> cur, nxt;
-  load_keys<D>(kp, t0 * WAVES * 64 + wave * 64, ui.L, cur);
+  const float c = a.scale_log2;
+  // lane (l & 31, l >> 5) keeps the statistics of row qb*32 + (l & 31) over its key half
+  float* my_m = sm.st_m + (wave * 2 + (lane >> 5)) * a.obs_pad + (lane & 31);
+  float* my_z = sm.st_z + (wave * 2 + (lane >> 5)) * a.obs_pad + (lane & 31);
+  KeyFrag<D> kf, kn;
+  load_keys<D>(kp, t0 * WAVES * 64 + wave * 64, ui.L, kf);
   __syncthreads();
-  float* my_m = sm.st_m + wave * a.obs_pad;
-  float* my_z = sm.st_z + wave * a.obs_pad;
   for (int t = t0; t < t1; ++t) {
     const int kbase = t * WAVES * 64 + wave * 64;
-    if (t + 1 < t1) load_keys<D>(kp, kbase + WAVES * 64, ui.L, nxt);
-    const bool full = kbase + 64 <= ui.L;
+    if (t + 1 < t1) load_keys<D>(kp, kbase + WAVES * 64, ui.L, kn);
     if (kbase < ui.L) {
+      const bool full = kbase + 64 <= ui.L;
+      bf16x8 qf[D / 16];
+      f32x16 acc[2];
+      load_qfrag<D>(sm.qs, 0, qf);
+      mfma_frags<D>(kf, qf, acc);
+      load_qfrag<D>(sm.qs, ui.nqb > 1 ? 1 : 0, qf);
+      if (!full) mask_tail(acc, kbase, ui.L, lane);
       for (int qb = 0; qb < ui.nqb; ++qb) {
-        f32x16 acc[2];
-        mfma_block<D>(cur, sm.qs, qb, acc);
-        float mx = kNegInf;
-        if (full) {
+        // The next block's products (qf already holds its rows) are issued step by step
+        // among this block's exponentials.  With the stale running max m the sum stays
+        // finite unless a logit exceeds m by ~64 (it is +inf/NaN while m is still -inf);
+        // then the exact update redoes the block.
+        float m = my_m[qb * 32], z = my_z[qb * 32];
+        const float neg = -m;
+        f32x16 n0 = {}, n1 = {};
+        float zs[4] = {0.f, 0.f, 0.f, 0.f};
+        constexpr int kPer = 32 / (D / 16);   // logits handled per MFMA step
 #pragma unroll
-          for (int f = 0; f < 2; ++f)
+        for (int st = 0; st < D / 16; ++st) {
+          n0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.v[0][st], qf[st], n0, 0, 0, 0);
+          n1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.v[1][st], qf[st], n1, 0, 0, 0);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[f][r]);
-        } else {
-#pragma unroll
-          for (int f = 0; f < 2; ++f)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const float x = kbase + acc_key(f, r, lane) < ui.L ? acc[f][r] : kNegInf;
-              acc[f][r] = x;
-              mx = fmaxf(mx, x);
-            }
+          for (int j = 0; j < kPer; ++j) {
+            const int idx = st * kPer + j;
+            zs[j & 3] += __builtin_amdgcn_exp2f(fmaf(acc[idx >> 4][idx & 15], c, neg));
+          }
         }
-        float m = mx * a.scale_log2;   // scale > 0 commutes with max
-        float z = 0.f;
-        if (mx != kNegInf) {
-          const float neg = -m;
+        // keep the two MFMAs of each step among this block's exp work
 #pragma unroll
-          for (int f = 0; f < 2; ++f)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) z += __builtin_amdgcn_exp2f(fmaf(acc[f][r], a.scale_log2, neg));
-        } else {
-          m = kNegInf;
+        for (int st = 0; st < D / 16; ++st) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);           // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x402, 3 * kPer, 0);    // VALU / transcendental
         }
-        merge_stats(m, z, __shfl_xor(m, 32), __shfl_xor(z, 32));
-        if (lane < 32) {
-          const int row = qb * 32 + lane;
-          float pm = my_m[row], pz = my_z[row];
-          merge_stats(pm, pz, m, z);
-          my_m[row] = pm;
-          my_z[row] = pz;
-        }
+        load_qfrag<D>(sm.qs, qb + 2 < ui.nqb ? qb + 2 : qb, qf);   // unconditional: one scheduling region
+        const float zt = (zs[0] + zs[1]) + (zs[2] + zs[3]);
+        if (zt <= 1.8e19f)   // 2^64: no term overflowed (false for NaN and +inf)
+          z += zt;
+        else
+          row_update_exact(acc, c, m, z);
+        my_m[qb * 32] = m;
+        my_z[qb * 32] = z;
+        acc[0] = n0;
+        acc[1] = n1;
+        if (!full) mask_tail(acc, kbase, ui.L, lane);
       }
     }
-    if (t + 1 < t1) cur = nxt;
+    if (t + 1 < t1) kf = kn;
   }
   __syncthreads();
   const size_t base = (static_cast<size_t>(u) * a.splits + split) * a.obs_pad;
   for (int i = threadIdx.x; i < ui.nqb * 32; i += blockDim.x) {
-    float m = sm.st_m[i], z = sm.st_z[i];
+    float m = kNegInf, z = 0.f;
 #pragma unroll
-    for (int w = 1; w < WAVES; ++w) merge_stats(m, z, sm.st_m[w * a.obs_pad + i], sm.st_z[w * a.obs_pad + i]);
+    for (int w = 0; w < 2 * WAVES; ++w) merge_stats(m, z, sm.st_m[w * a.obs_pad + i], sm.st_z[w * a.obs_pad + i]);
     a.part_m[base + i] = m;
     a.part_z[base + i] = z;
   }
@@ -241,15 +298,23 @@ __device__ void pass2_item(const ScoreArgs& a, int u, int split, const UnitInfo&
   const int t1 = min(t0 + a.tps, ui.ntiles);
   const uint16_t* kp = a.k[ui.layer] + (static_cast<size_t>(ui.b) * a.n_kv_heads + ui.h) * a.capacity * D;
   float* sp = a.scores[ui.layer] + (static_cast<size_t>(ui.b) * a.n_kv_heads + ui.h) * a.capacity;
-  KeyFrag<D> cur, nxt;
-  load_keys<D>(kp, t0 * WAVES * 64 + wave * 64, ui.L, cur);
+  KeyFrag<D> kf;   // no prefetch buffer: these keys were just read by the stats kernel
+  load_keys<D>(kp, t0 * WAVES * 64 + wave * 64, ui.L, kf);
   stage_queries<D>(a, ui, sm.qs);
-  // log2-sum-exp2 of every observation row from the unit's stats partials.
+  // log2-sum-exp2 of every observation row from the unit's stats partials (the loads of
+  // up to 8 splits are issued before any is used).
   for (int i = threadIdx.x; i < ui.nqb * 32; i += blockDim.x) {
     float M = kNegInf, Z = 0.f;
-    for (int sp_ = 0; sp_ < ui.nsplits; ++sp_) {
-      const size_t o = (static_cast<size_t>(u) * a.splits + sp_) * a.obs_pad + i;
-      merge_stats(M, Z, a.part_m[o], a.part_z[o]);
+    for (int s0 = 0; s0 < ui.nsplits; s0 += 8) {
+      float pm[8], pz[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const size_t o = (static_cast<size_t>(u) * a.splits + (s0 + j)) * a.obs_pad + i;
+        pm[j] = s0 + j < ui.nsplits ? a.part_m[o] : kNegInf;
+        pz[j] = s0 + j < ui.nsplits ? a.part_z[o] : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) merge_stats(M, Z, pm[j], pz[j]);
     }
     // Padding rows get +inf: they never win the max.
     sm.lse_s[i] = (i < ui.n_obs && Z > 0.f) ? M + log2f(Z) : kPosInf;
@@ -257,19 +322,38 @@ __device__ void pass2_item(const ScoreArgs& a, int u, int split, const UnitInfo&
   __syncthreads();
   for (int t = t0; t < t1; ++t) {
     const int kbase = t * WAVES * 64 + wave * 64;
-    if (t + 1 < t1) load_keys<D>(kp, kbase + WAVES * 64, ui.L, nxt);
+    if (t > t0) load_keys<D>(kp, kbase, ui.L, kf);
     if (kbase < ui.L) {
       float v[32];
 #pragma unroll
       for (int i = 0; i < 32; ++i) v[i] = kNegInf;
+      bf16x8 qf[D / 16];
+      f32x16 acc[2];
+      load_qfrag<D>(sm.qs, 0, qf);
+      mfma_frags<D>(kf, qf, acc);
+      load_qfrag<D>(sm.qs, ui.nqb > 1 ? 1 : 0, qf);
       for (int qb = 0; qb < ui.nqb; ++qb) {
-        f32x16 acc[2];
-        mfma_block<D>(cur, sm.qs, qb, acc);
         const float neg_lse = -sm.lse_s[qb * 32 + (lane & 31)];
+        f32x16 n0 = {}, n1 = {};
+        constexpr int kPer = 32 / (D / 16);
 #pragma unroll
-        for (int f = 0; f < 2; ++f)
+        for (int st = 0; st < D / 16; ++st) {
+          n0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.v[0][st], qf[st], n0, 0, 0, 0);
+          n1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.v[1][st], qf[st], n1, 0, 0, 0);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) v[f * 16 + r] = fmaxf(v[f * 16 + r], fmaf(acc[f][r], a.scale_log2, neg_lse));
+          for (int j = 0; j < kPer; ++j) {
+            const int idx = st * kPer + j;
+            v[idx] = fmaxf(v[idx], fmaf(acc[idx >> 4][idx & 15], a.scale_log2, neg_lse));
+          }
+        }
+#pragma unroll
+        for (int st = 0; st < D / 16; ++st) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);           // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 2 * kPer, 0);    // VALU
+        }
+        load_qfrag<D>(sm.qs, qb + 2 < ui.nqb ? qb + 2 : qb, qf);   // unconditional: one scheduling region
+        acc[0] = n0;
+        acc[1] = n1;
       }
       // Max over the 32 observation rows held by lanes l ^ {16,8,4,2,1}: each exchange
       // halves the values a lane keeps, so lane l ends with value index (l & 31).
@@ -287,7 +371,6 @@ __device__ void pass2_item(const ScoreArgs& a, int u, int split, const UnitInfo&
       const int key = kbase + acc_key(vi >> 4, vi & 15, lane);
       if (key < ui.L) sp[key] = ui.n_obs > 0 ? exp2f(v[0]) : 0.f;
     }
-    if (t + 1 < t1) cur = nxt;
   }
   __syncthreads();   // LDS is restaged by the next item
 }
@@ -310,7 +393,7 @@ __global__ __launch_bounds__(WAVES * 64) void score_kernel(const ScoreArgs a) {
 
 template <int D, int WAVES>
 size_t lds_bytes(int obs_pad) {
-  return static_cast<size_t>(obs_pad) * (D * 2 + 16) + 2 * WAVES * obs_pad * sizeof(float);
+  return static_cast<size_t>(obs_pad) * (D * 2 + 16) + 4 * WAVES * obs_pad * sizeof(float);
 }
 
 template <int D, int WAVES>
@@ -357,18 +440,13 @@ hipError_t launch_d(ScoreArgs a, hipStream_t s) {
 
 }  // namespace
 
-int score_waves(int obs_pad) { return obs_pad <= 384 ? 8 : 4; }
-
-size_t score_lds_bytes(int head_dim, int obs_pad) {
-  const int w = score_waves(obs_pad);
-  if (head_dim == 128) return w == 8 ? lds_bytes<128, 8>(obs_pad) : lds_bytes<128, 4>(obs_pad);
-  return w == 8 ? lds_bytes<64, 8>(obs_pad) : lds_bytes<64, 4>(obs_pad);
-}
+// Waves per workgroup so that the LDS (observation rows + per-wave statistics) fits in 160 KB.
+int score_waves(int obs_pad) { return obs_pad <= 288 ? 8 : (obs_pad <= 448 ? 4 : 2); }
 
 hipError_t launch_score(const ScoreArgs& a, int /*n_layers*/, int head_dim, hipStream_t s) {
   const int w = score_waves(a.obs_pad);
-  if (head_dim == 128) return w == 8 ? launch_d<128, 8>(a, s) : launch_d<128, 4>(a, s);
-  return w == 8 ? launch_d<64, 8>(a, s) : launch_d<64, 4>(a, s);
+  if (head_dim == 128) return w == 8 ? launch_d<128, 8>(a, s) : (w == 4 ? launch_d<128, 4>(a, s) : launch_d<128, 2>(a, s));
+  return w == 8 ? launch_d<64, 8>(a, s) : (w == 4 ? launch_d<64, 4>(a, s) : launch_d<64, 2>(a, s));
 }
 
 }  // namespace bkv
