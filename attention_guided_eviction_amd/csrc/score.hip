@@ -7,20 +7,22 @@
 // where lse_i normalises row i over all valid keys.  Everything runs in the log2
 // domain: t_ij = s_ij * log2(e) and score_j = exp2(max_i(t_ij - lse2_i)).
 //
-// Two kernels per chunk of units, each a grid-stride loop over items (unit, split); an
-// item is a run of key tiles of one unit.  No workgroup ever waits for another:
+// Two kernels, each one launch over every unit and a grid-stride loop over items
+// (unit, split); an item is a run of key tiles of one unit.  No workgroup ever waits for
+// another:
 //   score_stats   logits of the item's tiles against every observation row, per-row
 //                 running max and sum of exp2 -> partial (m, z) per (unit, split, row);
 //   score_finish  merges the unit's partials into lse2 per row (in LDS), recomputes
 //                 the logits and writes exp2(max_i(t_ij - lse2_i)) for its keys.
-// The host walks the units in chunks of at most ~128 MB of keys, stats then finish per
-// chunk, so the second read of a chunk's keys comes from the last-level cache.
+// Both passes are bound by the matrix and vector units rather than by HBM, so the keys
+// are simply read twice.
 //
 // MFMA mapping (v_mfma_f32_32x32x16_bf16): the A operand is 32 keys x 16 dims, the B
 // operand 16 dims x 32 observation rows, so one lane's 16 accumulators are 16 keys of
 // one observation row.  Row statistics reduce inside a lane; the per-key max is one
-// cross-lane reduction per key tile.  Key fragments for the next tile are loaded while
-// the current one is multiplied.
+// cross-lane reduction per key tile.  Four waves per workgroup, each owning 64 keys of
+// a 256-key tile; the exp2 work of one observation block is interleaved with the MFMAs
+// of the next.
 #include <algorithm>
 #include <mutex>
 
@@ -61,13 +63,13 @@ __device__ inline UnitInfo unit_info(const ScoreArgs& a, int u) {
   return ui;
 }
 
-// Stage the unit's observation rows in LDS (row stride D*2+16 bytes keeps the 16-byte
-// fragment reads of 8 consecutive rows on distinct banks); rows n_obs..nqb*32-1 are zero.
-// Each thread issues its loads in batches of 8 before waiting, so the staging costs about
-// one memory latency per batch rather than one per row chunk.
+// Stage the unit's observation rows in LDS, rows n_obs..nqb*32-1 zero.  Row r occupies
+// D*2 bytes with its 16-byte chunk c stored at chunk slot c ^ (r mod D/8): the fragment
+// reads of 16 consecutive rows at one chunk then touch 16 different slots, i.e. all 64
+// banks once, with no padding.  Each thread issues its loads in batches of 8 before
+// waiting, so staging costs about one memory latency per batch.
 template <int D>
 __device__ inline void stage_queries(const ScoreArgs& a, const UnitInfo& ui, uint8_t* qs) {
-  constexpr int kRowBytes = D * 2 + 16;
   constexpr int kChunks = D / 8;
   constexpr int kBatch = 8;
   const int gw = a.group * a.window;
@@ -98,7 +100,8 @@ __device__ inline void stage_queries(const ScoreArgs& a, const UnitInfo& ui, uin
     for (int j = 0; j < kBatch; ++j) {
       const int c = c0 + j * blockDim.x;
       const int r = c / kChunks;
-      if (c < total) *reinterpret_cast<uint4*>(qs + r * kRowBytes + (c - r * kChunks) * 16) = v[j];
+      const int cc = c - r * kChunks;
+      if (c < total) *reinterpret_cast<uint4*>(qs + r * (D * 2) + ((cc ^ (r & (kChunks - 1))) * 16)) = v[j];
     }
   }
 }
@@ -128,11 +131,14 @@ __device__ inline void load_keys(const uint16_t* kp, int kbase, int L, KeyFrag<D
 
 template <int D>
 __device__ inline void load_qfrag(const uint8_t* qs, int qb, bf16x8 (&qf)[D / 16]) {
-  constexpr int kRowBytes = D * 2 + 16;
+  constexpr int kChunks = D / 8;
   const int lane = threadIdx.x & 63;
-  const uint8_t* qrow = qs + (qb * 32 + (lane & 31)) * kRowBytes + (lane >> 5) * 16;
+  const int row = qb * 32 + (lane & 31);
+  const uint8_t* base = qs + row * (D * 2);
+  const int sw = row & (kChunks - 1);
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + s * 32);
+  for (int s = 0; s < D / 16; ++s)
+    qf[s] = *reinterpret_cast<const bf16x8*>(base + (((2 * s + (lane >> 5)) ^ sw) * 16));
 }
 
 template <int D>
@@ -162,7 +168,7 @@ __device__ inline void merge_stats(float& m, float& z, float m2, float z2) {
 
 template <int D, int WAVES>
 struct Smem {
-  static constexpr int kRowBytes = D * 2 + 16;
+  static constexpr int kRowBytes = D * 2;
   uint8_t* qs;
   float* st_m;   // [WAVES][2][obs_pad] (pass 1): per wave and lane half
   float* st_z;   // [WAVES][2][obs_pad] (pass 1)
@@ -376,7 +382,7 @@ __device__ void pass2_item(const ScoreArgs& a, int u, int split, const UnitInfo&
 }
 
 template <int D, int WAVES, bool FINISH>
-__global__ __launch_bounds__(WAVES * 64) void score_kernel(const ScoreArgs a) {
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 8))) void score_kernel(const ScoreArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int n_items = a.units * a.splits;
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
@@ -393,7 +399,7 @@ __global__ __launch_bounds__(WAVES * 64) void score_kernel(const ScoreArgs a) {
 
 template <int D, int WAVES>
 size_t lds_bytes(int obs_pad) {
-  return static_cast<size_t>(obs_pad) * (D * 2 + 16) + 4 * WAVES * obs_pad * sizeof(float);
+  return static_cast<size_t>(obs_pad) * (D * 2) + 4 * WAVES * obs_pad * sizeof(float);
 }
 
 template <int D, int WAVES>
@@ -419,11 +425,11 @@ hipError_t launch_d(ScoreArgs a, hipStream_t s) {
   const int resident = std::max(1, per_cu) * cus;
   a.tps = kScoreTilesPerItem;
   a.splits = score_splits(a.capacity, a.obs_pad);
-  // Chunks of whole units with at most ~128 MB of keys (half the last-level cache), so
-  // score_finish re-reads keys that score_stats has just brought in.
-  const long long unit_bytes = static_cast<long long>(a.capacity) * D * 2;
-  const int per_chunk = static_cast<int>(std::max(1ll, (128ll << 20) / std::max(1ll, unit_bytes)));
+  // One stats launch and one finish launch over every unit: the passes are bound by the
+  // matrix and vector units, not by memory (the finish pass re-reads the keys at a few
+  // TB/s), and every extra launch costs its ramp-up and tail.
   const int total_units = a.units;
+  const int per_chunk = total_units;
   for (int u0 = 0; u0 < total_units; u0 += per_chunk) {
     a.unit0 = u0;
     a.units = std::min(per_chunk, total_units - u0);
@@ -440,13 +446,14 @@ hipError_t launch_d(ScoreArgs a, hipStream_t s) {
 
 }  // namespace
 
-// Waves per workgroup so that the LDS (observation rows + per-wave statistics) fits in 160 KB.
-int score_waves(int obs_pad) { return obs_pad <= 288 ? 8 : (obs_pad <= 448 ? 4 : 2); }
+// Four waves per workgroup: the LDS (observation rows + per-wave statistics) is
+// obs_pad * (2D + 32) bytes, at most 160 KB, and up to 256 rows two workgroups share a CU.
+int score_waves(int /*obs_pad*/) { return 4; }
 
 hipError_t launch_score(const ScoreArgs& a, int /*n_layers*/, int head_dim, hipStream_t s) {
   const int w = score_waves(a.obs_pad);
-  if (head_dim == 128) return w == 8 ? launch_d<128, 8>(a, s) : (w == 4 ? launch_d<128, 4>(a, s) : launch_d<128, 2>(a, s));
-  return w == 8 ? launch_d<64, 8>(a, s) : (w == 4 ? launch_d<64, 4>(a, s) : launch_d<64, 2>(a, s));
+  (void)w;
+  return head_dim == 128 ? launch_d<128, 4>(a, s) : launch_d<64, 4>(a, s);
 }
 
 }  // namespace bkv
