@@ -69,13 +69,18 @@ struct ScoreWs {
   size_t part_bytes, total;
 };
 
+// Statistics partials of the largest launch: launches of kMaxLayers layers and one of the
+// remaining layers run one after another on the stream and reuse the workspace.
 ScoreWs score_ws(const bkv_shape* s, int window, int nb_max) {
   ScoreWs w{};
-  const size_t units = static_cast<size_t>(layers_per_launch(s)) * s->batch * s->n_kv_heads;
-  const int obs_pad = obs_pad_of(s, window, nb_max);
-  const size_t splits = static_cast<size_t>(score_splits(s->capacity, obs_pad));
-  const size_t obs = static_cast<size_t>(obs_pad);
-  w.part_bytes = align_up(units * splits * obs * sizeof(float));
+  const size_t obs = static_cast<size_t>(obs_pad_of(s, window, nb_max));
+  size_t cells = 0;
+  for (int nl : {layers_per_launch(s), s->n_layers % kMaxLayers}) {
+    if (nl == 0) continue;
+    const size_t units = static_cast<size_t>(nl) * s->batch * s->n_kv_heads;
+    cells = std::max(cells, units * static_cast<size_t>(score_slots(s->capacity, nl, s->n_kv_heads)));
+  }
+  w.part_bytes = align_up(cells * obs * sizeof(float));
   w.total = 2 * w.part_bytes;
   return w;
 }
@@ -200,7 +205,6 @@ bkv_status bkv_score(const bkv_shape* shape, const void* const* k, const void* c
   a.window = window;
   a.nb_max = nb_max;
   a.obs_pad = obs_pad_of(shape, window, nb_max);
-  a.tps = kScoreTilesPerItem;
   a.scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(shape->head_dim)));
   for (int l0 = 0; l0 < shape->n_layers; l0 += kMaxLayers) {
     const int nl = std::min(kMaxLayers, shape->n_layers - l0);
@@ -211,7 +215,6 @@ bkv_status bkv_score(const bkv_shape* shape, const void* const* k, const void* c
       a.n_beacons[i] = nb_max > 0 ? n_beacons[l0 + i] : nullptr;
       a.scores[i] = scores[l0 + i];
     }
-    a.units = nl * shape->batch * shape->n_kv_heads;
     st = hip_status(launch_score(a, nl, shape->head_dim, stream));
     if (st != BKV_OK) return st;
   }

@@ -14,9 +14,11 @@ namespace bkv {
 constexpr int kMaxLayers = 48;
 
 // ---- score ----------------------------------------------------------------------------------
-// Two grid-stride kernels per chunk of units (see score.hip).  Key tiles are WAVES*64 keys;
-// an item is kScoreTilesPerItem consecutive tiles of one unit.
-constexpr int kScoreTilesPerItem = 4;
+// Two persistent kernels (see score.hip).  A tile is kScoreTile keys of one unit; the grid is
+// at most kScoreMaxGrid workgroups, each taking an equal contiguous share of the launch's
+// tiles, so at most grid / (n_layers * n_kv_heads) + 2 workgroups share one unit.
+constexpr int kScoreTile = 256;
+constexpr int kScoreMaxGrid = 1024;
 
 struct ScoreArgs {
   const uint16_t* k[kMaxLayers];
@@ -25,25 +27,22 @@ struct ScoreArgs {
   const int32_t* n_beacons[kMaxLayers];
   float* scores[kMaxLayers];
   const int32_t* seq_len;
-  float* part_m;        // [unit][split][obs_pad] running max (log2 domain)
-  float* part_z;        // [unit][split][obs_pad] sum of exp2(t - m)
+  float* part_m;        // [unit][slot][obs_pad] running max (log2 domain)
+  float* part_z;        // [unit][slot][obs_pad] sum of exp2(t - m)
+  int n_layers;         // layers in this launch (set by the launcher)
   int batch, n_q_heads, n_kv_heads, group, capacity;
   int q_len, window, nb_max;
   int obs_pad;          // observation rows per unit rounded up to 32 (launch-wide)
-  int unit0;            // first unit of the current chunk (set by the launcher)
-  int units;            // units in the chunk (the whole call on entry to the launcher)
-  int tps;              // tiles per item
-  int splits;           // items per unit (set by the launcher)
+  int slots;            // statistics slots per unit (set by the launcher)
   float scale_log2;     // log2(e) / sqrt(head_dim)
 };
 
-// Waves per score workgroup for a given padded observation count, and the split count the
-// launcher will use (the workspace is sized from these).
-int score_waves(int obs_pad);
-inline int score_splits(int capacity, int obs_pad) {
-  const int tile = score_waves(obs_pad) * 64;
-  const int ntiles = (capacity + tile - 1) / tile;
-  return (ntiles + kScoreTilesPerItem - 1) / kScoreTilesPerItem;
+// Statistics slots per unit for a launch of n_layers layers (the workspace is sized from
+// this): one per workgroup that can share a unit, never more than the unit's tiles.
+inline int score_slots(int capacity, int n_layers, int n_kv_heads) {
+  const int tiles = (capacity + kScoreTile - 1) / kScoreTile;
+  const int sharing = kScoreMaxGrid / (n_layers * n_kv_heads) + 2;
+  return tiles < sharing ? tiles : sharing;
 }
 
 // ---- select ------------------------------------------------------------------------------

@@ -7,22 +7,27 @@
 // where lse_i normalises row i over all valid keys.  Everything runs in the log2
 // domain: t_ij = s_ij * log2(e) and score_j = exp2(max_i(t_ij - lse2_i)).
 //
-// Two kernels, each one launch over every unit and a grid-stride loop over items
-// (unit, split); an item is a run of key tiles of one unit.  No workgroup ever waits for
-// another:
-//   score_stats   logits of the item's tiles against every observation row, per-row
-//                 running max and sum of exp2 -> partial (m, z) per (unit, split, row);
+// Two persistent kernels.  The launch's key tiles (256 keys each, unit after unit) are
+// cut into one contiguous, equal share per workgroup; a share covers the end of one unit,
+// whole units and the start of another.  Per unit piece ("segment") a workgroup stages
+// the unit's observation rows in LDS once and then walks its tiles.  No workgroup ever
+// waits for another:
+//   score_stats   per-row running max and sum of exp2 over the segment's keys ->
+//                 one partial (m, z) per (unit, segment) and row;
 //   score_finish  merges the unit's partials into lse2 per row (in LDS), recomputes
 //                 the logits and writes exp2(max_i(t_ij - lse2_i)) for its keys.
 // Both passes are bound by the matrix and vector units rather than by HBM, so the keys
-// are simply read twice.
+// are simply read twice.  The segments of a unit are numbered by workgroup: the
+// workgroup holding global tile c is the last w with floor(w N / G) <= c, i.e.
+// ceil((c + 1) G / N) - 1 for N tiles over G workgroups, so the finish pass finds every
+// partial of a unit without any table.
 //
-// MFMA mapping (v_mfma_f32_32x32x16_bf16): the A operand is 32 keys x 16 dims, the B
-// operand 16 dims x 32 observation rows, so one lane's 16 accumulators are 16 keys of
-// one observation row.  Row statistics reduce inside a lane; the per-key max is one
-// cross-lane reduction per key tile.  Four waves per workgroup, each owning 64 keys of
-// a 256-key tile; the exp2 work of one observation block is interleaved with the MFMAs
-// of the next.
+// MFMA mapping (v_mfma_f32_32x32x16_bf16, four waves, each owning 64 keys of a tile).
+// Stats pass: A = 32 keys x 16 dims, B = 16 dims x 32 observation rows, so a lane's 16
+// accumulators are 16 keys of one row and the row sums reduce inside the lane.  Finish
+// pass: A = rows, B = keys, so a lane's accumulators are 16 rows of one key and the max
+// over rows reduces inside the lane.  Blocks of 32 rows run two at a time in ping-pong
+// accumulators: the products of one block are issued among the vector work of the other.
 #include <algorithm>
 #include <mutex>
 
@@ -34,14 +39,107 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+static_assert(kScoreTile == kWaves * 64, "a tile is 64 keys per wave");
+
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kPosInf = __builtin_inff();
 
-struct UnitInfo {
-  int layer, b, h, L, n_obs, nqb, ntiles, nsplits;
+// ---- work split -----------------------------------------------------------------------
+
+__device__ inline int seq_tiles(const ScoreArgs& a, int b) {
+  int L = a.seq_len[b];
+  L = L < 0 ? 0 : (L > a.capacity ? a.capacity : L);
+  return (L + kScoreTile - 1) / kScoreTile;
+}
+
+__device__ inline int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Tiles of one layer, all sequences and KV heads (computed by every wave).
+__device__ inline int layer_tiles(const ScoreArgs& a) {
+  const int lane = threadIdx.x & 63;
+  int s = 0;
+  for (int b0 = 0; b0 < a.batch; b0 += 64) {
+    int x = b0 + lane < a.batch ? seq_tiles(a, b0 + lane) : 0;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+    s += x;
+  }
+  return uniform(s * a.n_kv_heads);
+}
+
+struct Cursor {
+  int u;      // unit (layer, sequence, KV head) of the launch
+  int tile;   // tile within the unit
+  int nt;     // tiles of the unit
 };
 
-template <int WAVES>
+// Unit and tile of global tile c (0 <= c < n_layers * T, T tiles per layer).
+__device__ inline Cursor locate(const ScoreArgs& a, long long c, int T) {
+  const int lane = threadIdx.x & 63;
+  const int layer = static_cast<int>(c / T);
+  const int r = static_cast<int>(c - static_cast<long long>(layer) * T);
+  // the sequence b with H * S_b <= r < H * S_{b+1}, S_b = tiles of sequences before b
+  int base = 0, b = 0, nt = 1, sb = 0;
+  for (int b0 = 0; b0 < a.batch; b0 += 64) {
+    const int x = b0 + lane < a.batch ? seq_tiles(a, b0 + lane) : 0;
+    int incl = x;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    const unsigned long long hit = __ballot((base + incl) * a.n_kv_heads > r);
+    if (hit) {
+      const int j = __ffsll(static_cast<long long>(hit)) - 1;
+      nt = __shfl(x, j);
+      sb = base + __shfl(incl, j) - nt;
+      b = b0 + j;
+      break;
+    }
+    base += __shfl(incl, 63);
+  }
+  const int rr = r - sb * a.n_kv_heads;
+  Cursor cur;
+  cur.nt = uniform(nt);
+  const int h = rr / cur.nt;
+  cur.tile = uniform(rr - h * cur.nt);
+  cur.u = uniform((layer * a.batch + b) * a.n_kv_heads + h);
+  return cur;
+}
+
+// Move to the first tile of the next unit that has keys; false past the launch's units
+// (never reached while the share has tiles left).
+__device__ inline bool next_unit(const ScoreArgs& a, Cursor& cur) {
+  const int units = a.n_layers * a.batch * a.n_kv_heads;
+  int u = cur.u + 1;
+  while (u < units) {
+    const int b = (u / a.n_kv_heads) % a.batch;
+    const int nt = seq_tiles(a, b);
+    if (nt > 0) {
+      cur.u = u;
+      cur.nt = nt;
+      cur.tile = 0;
+      return true;
+    }
+    u = (u / a.n_kv_heads + 1) * a.n_kv_heads;   // the whole sequence is empty
+  }
+  return false;
+}
+
+// Workgroup whose share holds global tile c.
+__device__ inline int owner(long long c, long long N, int G) {
+  return static_cast<int>(((c + 1) * G + N - 1) / N - 1);
+}
+
+
+// ---- per-unit data ------------------------------------------------------------------------
+
+struct UnitInfo {
+  int layer, b, h, L, n_obs, nqb;
+};
+
 __device__ inline UnitInfo unit_info(const ScoreArgs& a, int u) {
   UnitInfo ui;
   const int per_layer = a.batch * a.n_kv_heads;
@@ -56,10 +154,8 @@ __device__ inline UnitInfo unit_info(const ScoreArgs& a, int u) {
     nb = a.n_beacons[ui.layer][ui.b * a.n_kv_heads + ui.h];
     nb = nb < 0 ? 0 : (nb > a.nb_max ? a.nb_max : nb);
   }
-  ui.n_obs = a.group * a.window + nb;
+  ui.n_obs = uniform(a.group * a.window + nb);
   ui.nqb = (ui.n_obs + 31) >> 5;
-  ui.ntiles = (ui.L + WAVES * 64 - 1) / (WAVES * 64);
-  ui.nsplits = (ui.ntiles + a.tps - 1) / a.tps;
   return ui;
 }
 
@@ -76,11 +172,11 @@ __device__ inline void stage_queries(const ScoreArgs& a, const UnitInfo& ui, uin
   const uint16_t* q = a.q[ui.layer];
   const uint16_t* bc = a.nb_max > 0 ? a.beacons[ui.layer] : nullptr;
   const int total = ui.nqb * 32 * kChunks;
-  for (int c0 = threadIdx.x; c0 < total; c0 += kBatch * blockDim.x) {
+  for (int c0 = threadIdx.x; c0 < total; c0 += kBatch * kThreads) {
     uint4 v[kBatch];
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
-      const int c = c0 + j * blockDim.x;
+      const int c = c0 + j * kThreads;
       const int r = c / kChunks;
       const int cc = c - r * kChunks;
       v[j] = make_uint4(0, 0, 0, 0);
@@ -98,7 +194,7 @@ __device__ inline void stage_queries(const ScoreArgs& a, const UnitInfo& ui, uin
     }
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
-      const int c = c0 + j * blockDim.x;
+      const int c = c0 + j * kThreads;
       const int r = c / kChunks;
       const int cc = c - r * kChunks;
       if (c < total) *reinterpret_cast<uint4*>(qs + r * (D * 2) + ((cc ^ (r & (kChunks - 1))) * 16)) = v[j];
@@ -106,9 +202,12 @@ __device__ inline void stage_queries(const ScoreArgs& a, const UnitInfo& ui, uin
   }
 }
 
-// Two 32-key A fragments.  Lane l holds key (l & 31) of each fragment and, for k-step
-// s, dims 16*s + 8*(l >> 5) .. +7.  Keys past the valid length read row L-1 (always in
-// bounds) and are masked by the caller.
+// ---- fragments --------------------------------------------------------------------------
+
+// Two 32-key fragments.  Lane l holds key (l & 31) of each fragment and, for k-step s,
+// dims 16*s + 8*(l >> 5) .. +7 (the A layout of keys in the stats pass and the B layout
+// in the finish pass are the same registers).  Keys past the valid length read row L-1
+// (always in bounds) and are masked or dropped by the caller.
 template <int D>
 struct KeyFrag {
   bf16x8 v[2][D / 16];
@@ -129,6 +228,8 @@ __device__ inline void load_keys(const uint16_t* kp, int kbase, int L, KeyFrag<D
   }
 }
 
+// Observation rows qb*32 .. +31 from LDS: lane l holds row (l & 31), dims of k-step s at
+// 16*s + 8*(l >> 5).
 template <int D>
 __device__ inline void load_qfrag(const uint8_t* qs, int qb, bf16x8 (&qf)[D / 16]) {
   constexpr int kChunks = D / 8;
@@ -141,23 +242,6 @@ __device__ inline void load_qfrag(const uint8_t* qs, int qb, bf16x8 (&qf)[D / 16
     qf[s] = *reinterpret_cast<const bf16x8*>(base + (((2 * s + (lane >> 5)) ^ sw) * 16));
 }
 
-template <int D>
-__device__ inline void mfma_frags(const KeyFrag<D>& kf, const bf16x8 (&qf)[D / 16], f32x16 (&acc)[2]) {
-  f32x16 c0 = {}, c1 = {};
-#pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.v[0][s], qf[s], c0, 0, 0, 0);
-    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.v[1][s], qf[s], c1, 0, 0, 0);
-  }
-  acc[0] = c0;
-  acc[1] = c1;
-}
-
-// Key offset (within the wave's 64 keys) of accumulator r of fragment f in lane l.
-__device__ inline int acc_key(int f, int r, int lane) {
-  return f * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-}
-
 // Merge two (max, sum) pairs of exp2 statistics.
 __device__ inline void merge_stats(float& m, float& z, float m2, float z2) {
   const float M = fmaxf(m, m2);
@@ -166,20 +250,27 @@ __device__ inline void merge_stats(float& m, float& z, float m2, float z2) {
   m = M;
 }
 
-template <int D, int WAVES>
+template <int D>
 struct Smem {
-  static constexpr int kRowBytes = D * 2;
-  uint8_t* qs;
-  float* st_m;   // [WAVES][2][obs_pad] (pass 1): per wave and lane half
-  float* st_z;   // [WAVES][2][obs_pad] (pass 1)
-  float* lse_s;  // [obs_pad]        (pass 2; aliases st_m)
+  uint8_t* qs;   // [obs_pad][D] bf16, swizzled
+  float* st_m;   // [kWaves][2][obs_pad] (stats pass): per wave and lane half
+  float* st_z;   // [kWaves][2][obs_pad] (stats pass)
+  float* lse_s;  // [obs_pad]            (finish pass; aliases st_m)
   __device__ Smem(uint8_t* base, int obs_pad) {
     qs = base;
-    st_m = reinterpret_cast<float*>(base + obs_pad * kRowBytes);
-    st_z = st_m + 2 * WAVES * obs_pad;
+    st_m = reinterpret_cast<float*>(base + obs_pad * (D * 2));
+    st_z = st_m + 2 * kWaves * obs_pad;
     lse_s = st_m;
   }
 };
+
+// ---- stats pass -------------------------------------------------------------------------
+
+// Key offset (within the wave's 64 keys) of accumulator r of fragment f in lane l, for the
+// stats layout (keys down the accumulator registers).
+__device__ inline int stats_key(int f, int r, int lane) {
+  return f * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+}
 
 // Keys at or past L (only in a unit's last tile) get -inf logits.
 __device__ inline void mask_tail(f32x16 (&acc)[2], int kbase, int L, int lane) {
@@ -187,11 +278,11 @@ __device__ inline void mask_tail(f32x16 (&acc)[2], int kbase, int L, int lane) {
   for (int f = 0; f < 2; ++f)
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-      if (kbase + acc_key(f, r, lane) >= L) acc[f][r] = kNegInf;
+      if (kbase + stats_key(f, r, lane) >= L) acc[f][r] = kNegInf;
 }
 
 // Exact (max, sum) update of one lane's 32 logits of one row: the block max is taken and
-// the running sum rescaled.  Used for a row's first block and when the cheap update below
+// the running sum rescaled.  Used for a row's first block and when the cheap update
 // reports a possible overflow.
 __device__ inline void row_update_exact(const f32x16 (&acc)[2], float c, float& m, float& z) {
   float mx = kNegInf;
@@ -211,113 +302,270 @@ __device__ inline void row_update_exact(const f32x16 (&acc)[2], float c, float& 
   m = mt;
 }
 
-template <int D, int WAVES>
-__device__ void pass1_item(const ScoreArgs& a, int u, int split, const UnitInfo& ui, uint8_t* smem) {
-  Smem<D, WAVES> sm(smem, a.obs_pad);
+// With the running max m of earlier blocks the sum stays finite unless a logit exceeds
+// m by ~64 (it is +inf/NaN while m is still -inf); then the exact update redoes the block.
+__device__ inline void stats_commit(const f32x16 (&cur)[2], float zt, float c, float* pm, float* pz) {
+  float m = *pm, z = *pz;
+  if (zt <= 1.8e19f)   // 2^64: no term overflowed (false for NaN and +inf)
+    z += zt;
+  else
+    row_update_exact(cur, c, m, z);
+  *pm = m;
+  *pz = z;
+}
+
+// Sum of exp2(c * x - m) over the block in `cur` while the products of the next block
+// go into `nxt`; then rows nq*32.. are loaded into qf.
+template <int D, bool MASK>
+__device__ inline void stats_step(const KeyFrag<D>& kf, bf16x8 (&qf)[D / 16], f32x16 (&cur)[2], f32x16 (&nxt)[2],
+                                  const uint8_t* qs, int nq, float c, float* pm, float* pz, int kbase, int L) {
+  const int lane = threadIdx.x & 63;
+  if (MASK) mask_tail(cur, kbase, L, lane);
+  const float neg = -*pm;
+  f32x16 n0 = {}, n1 = {};
+  float zs[4] = {0.f, 0.f, 0.f, 0.f};
+  constexpr int kPer = 32 / (D / 16);   // logits handled per MFMA step
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) {
+    n0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.v[0][st], qf[st], n0, 0, 0, 0);
+    n1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.v[1][st], qf[st], n1, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int idx = st * kPer + j;
+      zs[j & 3] += __builtin_amdgcn_exp2f(fmaf(cur[idx >> 4][idx & 15], c, neg));
+    }
+  }
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);           // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x402, 3 * kPer, 0);    // VALU / transcendental
+  }
+  load_qfrag<D>(qs, nq, qf);
+  stats_commit(cur, (zs[0] + zs[1]) + (zs[2] + zs[3]), c, pm, pz);
+  nxt[0] = n0;
+  nxt[1] = n1;
+}
+
+// The last block of a tile: no products left to overlap.
+template <bool MASK>
+__device__ inline void stats_last(f32x16 (&cur)[2], float c, float* pm, float* pz, int kbase, int L) {
+  const int lane = threadIdx.x & 63;
+  if (MASK) mask_tail(cur, kbase, L, lane);
+  const float neg = -*pm;
+  float zs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int idx = 0; idx < 32; ++idx) zs[idx & 3] += __builtin_amdgcn_exp2f(fmaf(cur[idx >> 4][idx & 15], c, neg));
+  stats_commit(cur, (zs[0] + zs[1]) + (zs[2] + zs[3]), c, pm, pz);
+}
+
+// One wave's 64 keys against all nqb >= 1 row blocks.  pm/pz address the lane's
+// statistics of row block 0; block qb is at +qb*32.
+template <int D, bool MASK>
+__device__ inline void stats_tile(const KeyFrag<D>& kf, const uint8_t* qs, int nqb, float c, float* pm, float* pz,
+                                  int kbase, int L) {
+  bf16x8 qf[D / 16];
+  f32x16 A[2], B[2];
+  load_qfrag<D>(qs, 0, qf);
+  {
+    f32x16 c0 = {}, c1 = {};
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.v[0][s], qf[s], c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.v[1][s], qf[s], c1, 0, 0, 0);
+    }
+    A[0] = c0;
+    A[1] = c1;
+  }
+  load_qfrag<D>(qs, nqb > 1 ? 1 : 0, qf);
+  int qb = 0;
+  for (; qb + 2 < nqb; qb += 2) {
+    stats_step<D, MASK>(kf, qf, A, B, qs, qb + 2, c, pm + qb * 32, pz + qb * 32, kbase, L);
+    stats_step<D, MASK>(kf, qf, B, A, qs, qb + 3 < nqb ? qb + 3 : nqb - 1, c, pm + (qb + 1) * 32,
+                        pz + (qb + 1) * 32, kbase, L);
+  }
+  if (qb + 1 < nqb) {
+    stats_step<D, MASK>(kf, qf, A, B, qs, qb + 1, c, pm + qb * 32, pz + qb * 32, kbase, L);
+    stats_last<MASK>(B, c, pm + (qb + 1) * 32, pz + (qb + 1) * 32, kbase, L);
+  } else {
+    stats_last<MASK>(A, c, pm + qb * 32, pz + qb * 32, kbase, L);
+  }
+}
+
+// Tiles tile0 .. tile0+ntile-1 of one unit -> partial statistics out_m/out_z [nqb*32].
+template <int D>
+__device__ void stats_segment(const ScoreArgs& a, const UnitInfo& ui, int tile0, int ntile, float* out_m,
+                              float* out_z, uint8_t* smem) {
+  Smem<D> sm(smem, a.obs_pad);
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
+  const uint16_t* kp = a.k[ui.layer] + (static_cast<size_t>(ui.b) * a.n_kv_heads + ui.h) * a.capacity * D;
+  // No register prefetch of the next tile: two waves share each SIMD and a tile's work
+  // (several microseconds) covers the other wave's load latency, while 64 more
+  // registers per lane would force spills.
+  KeyFrag<D> kf;
+  load_keys<D>(kp, tile0 * kScoreTile + wave * 64, ui.L, kf);
   stage_queries<D>(a, ui, sm.qs);
-  for (int i = threadIdx.x; i < 2 * WAVES * a.obs_pad; i += blockDim.x) {
+  for (int i = threadIdx.x; i < 2 * kWaves * a.obs_pad; i += kThreads) {
     sm.st_m[i] = kNegInf;
     sm.st_z[i] = 0.f;
   }
-  const int t0 = split * a.tps;
-  const int t1 = min(t0 + a.tps, ui.ntiles);
-  const uint16_t* kp = a.k[ui.layer] + (static_cast<size_t>(ui.b) * a.n_kv_heads + ui.h) * a.capacity * D;
   const float c = a.scale_log2;
   // lane (l & 31, l >> 5) keeps the statistics of row qb*32 + (l & 31) over its key half
   float* my_m = sm.st_m + (wave * 2 + (lane >> 5)) * a.obs_pad + (lane & 31);
   float* my_z = sm.st_z + (wave * 2 + (lane >> 5)) * a.obs_pad + (lane & 31);
-  KeyFrag<D> kf, kn;
-  load_keys<D>(kp, t0 * WAVES * 64 + wave * 64, ui.L, kf);
   __syncthreads();
-  for (int t = t0; t < t1; ++t) {
-    const int kbase = t * WAVES * 64 + wave * 64;
-    if (t + 1 < t1) load_keys<D>(kp, kbase + WAVES * 64, ui.L, kn);
-    if (kbase < ui.L) {
-      const bool full = kbase + 64 <= ui.L;
-      bf16x8 qf[D / 16];
-      f32x16 acc[2];
-      load_qfrag<D>(sm.qs, 0, qf);
-      mfma_frags<D>(kf, qf, acc);
-      load_qfrag<D>(sm.qs, ui.nqb > 1 ? 1 : 0, qf);
-      if (!full) mask_tail(acc, kbase, ui.L, lane);
-      for (int qb = 0; qb < ui.nqb; ++qb) {
-        // The next block's products (qf already holds its rows) are issued step by step
-        // among this block's exponentials.  With the stale running max m the sum stays
-        // finite unless a logit exceeds m by ~64 (it is +inf/NaN while m is still -inf);
-        // then the exact update redoes the block.
-        float m = my_m[qb * 32], z = my_z[qb * 32];
-        const float neg = -m;
-        f32x16 n0 = {}, n1 = {};
-        float zs[4] = {0.f, 0.f, 0.f, 0.f};
-        constexpr int kPer = 32 / (D / 16);   // logits handled per MFMA step
-#pragma unroll
-        for (int st = 0; st < D / 16; ++st) {
-          n0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.v[0][st], qf[st], n0, 0, 0, 0);
-          n1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.v[1][st], qf[st], n1, 0, 0, 0);
-#pragma unroll
-          for (int j = 0; j < kPer; ++j) {
-            const int idx = st * kPer + j;
-            zs[j & 3] += __builtin_amdgcn_exp2f(fmaf(acc[idx >> 4][idx & 15], c, neg));
-          }
-        }
-        // keep the two MFMAs of each step among this block's exp work
-#pragma unroll
-        for (int st = 0; st < D / 16; ++st) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);           // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x402, 3 * kPer, 0);    // VALU / transcendental
-        }
-        load_qfrag<D>(sm.qs, qb + 2 < ui.nqb ? qb + 2 : qb, qf);   // unconditional: one scheduling region
-        const float zt = (zs[0] + zs[1]) + (zs[2] + zs[3]);
-        if (zt <= 1.8e19f)   // 2^64: no term overflowed (false for NaN and +inf)
-          z += zt;
-        else
-          row_update_exact(acc, c, m, z);
-        my_m[qb * 32] = m;
-        my_z[qb * 32] = z;
-        acc[0] = n0;
-        acc[1] = n1;
-        if (!full) mask_tail(acc, kbase, ui.L, lane);
-      }
+  const int t1 = tile0 + ntile;
+  for (int t = tile0; t < t1; ++t) {
+    const int kbase = t * kScoreTile + wave * 64;
+    if (t > tile0) load_keys<D>(kp, kbase, ui.L, kf);
+    if (kbase < ui.L && ui.nqb > 0) {
+      if (kbase + 64 <= ui.L)
+        stats_tile<D, false>(kf, sm.qs, ui.nqb, c, my_m, my_z, kbase, ui.L);
+      else
+        stats_tile<D, true>(kf, sm.qs, ui.nqb, c, my_m, my_z, kbase, ui.L);
     }
-    if (t + 1 < t1) kf = kn;
   }
   __syncthreads();
-  const size_t base = (static_cast<size_t>(u) * a.splits + split) * a.obs_pad;
-  for (int i = threadIdx.x; i < ui.nqb * 32; i += blockDim.x) {
+  for (int i = threadIdx.x; i < ui.nqb * 32; i += kThreads) {
     float m = kNegInf, z = 0.f;
 #pragma unroll
-    for (int w = 0; w < 2 * WAVES; ++w) merge_stats(m, z, sm.st_m[w * a.obs_pad + i], sm.st_z[w * a.obs_pad + i]);
-    a.part_m[base + i] = m;
-    a.part_z[base + i] = z;
+    for (int w = 0; w < 2 * kWaves; ++w) merge_stats(m, z, sm.st_m[w * a.obs_pad + i], sm.st_z[w * a.obs_pad + i]);
+    out_m[i] = m;
+    out_z[i] = z;
   }
-  __syncthreads();   // LDS is restaged by the next item
+  __syncthreads();   // LDS is restaged by the next segment
 }
 
-template <int D, int WAVES>
-__device__ void pass2_item(const ScoreArgs& a, int u, int split, const UnitInfo& ui, uint8_t* smem) {
-  Smem<D, WAVES> sm(smem, a.obs_pad);
+// ---- finish pass ------------------------------------------------------------------------
+
+// Row log2-sum-exp2 for the rows a lane's accumulators hold in the finish layout: register
+// r = 4g + j of lane l is row 8g + 4(l >> 5) + j of the block.
+struct RowLse {
+  float4 g[4];
+};
+
+__device__ inline void load_lse(const float* lse_s, int qb, RowLse& out) {
+  const int lane = threadIdx.x & 63;
+  const float* p = lse_s + qb * 32 + 4 * (lane >> 5);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) out.g[g] = *reinterpret_cast<const float4*>(p + 8 * g);
+}
+
+__device__ inline float lse_at(const RowLse& l, int r) {
+  const float4 v = l.g[r >> 2];
+  return (r & 3) == 0 ? v.x : (r & 3) == 1 ? v.y : (r & 3) == 2 ? v.z : v.w;
+}
+
+// Running max over rows of c * x - lse for the block in `cur` (fragment f in vm[f]) while
+// the products of the next block go into `nxt`; then rows nq*32.. are loaded into qf and
+// the next block's lse into lnext.
+template <int D>
+__device__ inline void finish_step(const KeyFrag<D>& kf, bf16x8 (&qf)[D / 16], const f32x16 (&cur)[2],
+                                   f32x16 (&nxt)[2], const RowLse& lcur, RowLse& lnext, const uint8_t* qs,
+                                   const float* lse_s, int qb_next, int nq, float c, float (&vm)[2]) {
+  f32x16 n0 = {}, n1 = {};
+  constexpr int kPer = 16 / (D / 16);   // (row, key) pairs of each fragment per MFMA step
+  load_lse(lse_s, qb_next, lnext);
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) {
+    n0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[st], kf.v[0][st], n0, 0, 0, 0);
+    n1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[st], kf.v[1][st], n1, 0, 0, 0);
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int j = 0; j < kPer; j += 2) {
+        const int r = st * kPer + j;
+        const float t0 = fmaf(cur[f][r], c, -lse_at(lcur, r));
+        const float t1 = fmaf(cur[f][r + 1], c, -lse_at(lcur, r + 1));
+        vm[f] = fmaxf(vm[f], fmaxf(t0, t1));
+      }
+  }
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);           // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 3 * kPer, 0);    // VALU
+  }
+  load_qfrag<D>(qs, nq, qf);
+  nxt[0] = n0;
+  nxt[1] = n1;
+}
+
+__device__ inline void finish_last(const f32x16 (&cur)[2], const RowLse& lcur, float c, float (&vm)[2]) {
+#pragma unroll
+  for (int f = 0; f < 2; ++f)
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const float t0 = fmaf(cur[f][r], c, -lse_at(lcur, r));
+      const float t1 = fmaf(cur[f][r + 1], c, -lse_at(lcur, r + 1));
+      vm[f] = fmaxf(vm[f], fmaxf(t0, t1));
+    }
+}
+
+// One wave's 64 keys: returns, in lane l, max over all rows of c * s - lse for key l of
+// the wave (fragment l >> 5, key l & 31).
+template <int D>
+__device__ inline float finish_tile(const KeyFrag<D>& kf, const uint8_t* qs, const float* lse_s, int nqb, float c) {
+  const int lane = threadIdx.x & 63;
+  float vm[2] = {kNegInf, kNegInf};
+  bf16x8 qf[D / 16];
+  f32x16 A[2], B[2];
+  RowLse la, lb;
+  load_qfrag<D>(qs, 0, qf);
+  load_lse(lse_s, 0, la);
+  {
+    f32x16 c0 = {}, c1 = {};
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[s], kf.v[0][s], c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[s], kf.v[1][s], c1, 0, 0, 0);
+    }
+    A[0] = c0;
+    A[1] = c1;
+  }
+  load_qfrag<D>(qs, nqb > 1 ? 1 : 0, qf);
+  int qb = 0;
+  for (; qb + 2 < nqb; qb += 2) {
+    finish_step<D>(kf, qf, A, B, la, lb, qs, lse_s, qb + 1, qb + 2, c, vm);
+    finish_step<D>(kf, qf, B, A, lb, la, qs, lse_s, qb + 2, qb + 3 < nqb ? qb + 3 : nqb - 1, c, vm);
+  }
+  if (qb + 1 < nqb) {
+    finish_step<D>(kf, qf, A, B, la, lb, qs, lse_s, qb + 1, qb + 1, c, vm);
+    finish_last(B, lb, c, vm);
+  } else {
+    finish_last(A, la, c, vm);
+  }
+  // lanes l and l ^ 32 hold the two row halves of the same keys
+  const bool lo = lane < 32;
+  const float keep = lo ? vm[0] : vm[1];
+  const float send = lo ? vm[1] : vm[0];
+  return fmaxf(keep, __shfl_xor(send, 32));
+}
+
+// Scores of tiles tile0 .. tile0+ntile-1 of one unit.  Its statistics partials are the
+// n_part slots at pm0/pz0 (stride obs_pad), slot s written by workgroup w0 + s.
+template <int D>
+__device__ void finish_segment(const ScoreArgs& a, const UnitInfo& ui, int tile0, int ntile, const float* pm0,
+                               const float* pz0, int n_part, uint8_t* smem) {
+  Smem<D> sm(smem, a.obs_pad);
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int t0 = split * a.tps;
-  const int t1 = min(t0 + a.tps, ui.ntiles);
   const uint16_t* kp = a.k[ui.layer] + (static_cast<size_t>(ui.b) * a.n_kv_heads + ui.h) * a.capacity * D;
   float* sp = a.scores[ui.layer] + (static_cast<size_t>(ui.b) * a.n_kv_heads + ui.h) * a.capacity;
-  KeyFrag<D> kf;   // no prefetch buffer: these keys were just read by the stats kernel
-  load_keys<D>(kp, t0 * WAVES * 64 + wave * 64, ui.L, kf);
+  KeyFrag<D> kf;
+  load_keys<D>(kp, tile0 * kScoreTile + wave * 64, ui.L, kf);
   stage_queries<D>(a, ui, sm.qs);
-  // log2-sum-exp2 of every observation row from the unit's stats partials (the loads of
-  // up to 8 splits are issued before any is used).
-  for (int i = threadIdx.x; i < ui.nqb * 32; i += blockDim.x) {
+  // log2-sum-exp2 of every observation row from the unit's partials (the loads of up to
+  // 8 slots are issued before any is used; slots of workgroups with no tiles are skipped).
+  for (int i = threadIdx.x; i < ui.nqb * 32; i += kThreads) {
     float M = kNegInf, Z = 0.f;
-    for (int s0 = 0; s0 < ui.nsplits; s0 += 8) {
+    for (int s0 = 0; s0 < n_part; s0 += 8) {
       float pm[8], pz[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const size_t o = (static_cast<size_t>(u) * a.splits + (s0 + j)) * a.obs_pad + i;
-        pm[j] = s0 + j < ui.nsplits ? a.part_m[o] : kNegInf;
-        pz[j] = s0 + j < ui.nsplits ? a.part_z[o] : 0.f;
+        const bool use = s0 + j < n_part;
+        const size_t o = static_cast<size_t>(s0 + j) * a.obs_pad + i;
+        pm[j] = use ? pm0[o] : kNegInf;
+        pz[j] = use ? pz0[o] : 0.f;
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) merge_stats(M, Z, pm[j], pz[j]);
@@ -326,134 +574,101 @@ __device__ void pass2_item(const ScoreArgs& a, int u, int split, const UnitInfo&
     sm.lse_s[i] = (i < ui.n_obs && Z > 0.f) ? M + log2f(Z) : kPosInf;
   }
   __syncthreads();
-  for (int t = t0; t < t1; ++t) {
-    const int kbase = t * WAVES * 64 + wave * 64;
-    if (t > t0) load_keys<D>(kp, kbase, ui.L, kf);
+  const int t1 = tile0 + ntile;
+  for (int t = tile0; t < t1; ++t) {
+    const int kbase = t * kScoreTile + wave * 64;
+    if (t > tile0) load_keys<D>(kp, kbase, ui.L, kf);
     if (kbase < ui.L) {
-      float v[32];
-#pragma unroll
-      for (int i = 0; i < 32; ++i) v[i] = kNegInf;
-      bf16x8 qf[D / 16];
-      f32x16 acc[2];
-      load_qfrag<D>(sm.qs, 0, qf);
-      mfma_frags<D>(kf, qf, acc);
-      load_qfrag<D>(sm.qs, ui.nqb > 1 ? 1 : 0, qf);
-      for (int qb = 0; qb < ui.nqb; ++qb) {
-        const float neg_lse = -sm.lse_s[qb * 32 + (lane & 31)];
-        f32x16 n0 = {}, n1 = {};
-        constexpr int kPer = 32 / (D / 16);
-#pragma unroll
-        for (int st = 0; st < D / 16; ++st) {
-          n0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.v[0][st], qf[st], n0, 0, 0, 0);
-          n1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.v[1][st], qf[st], n1, 0, 0, 0);
-#pragma unroll
-          for (int j = 0; j < kPer; ++j) {
-            const int idx = st * kPer + j;
-            v[idx] = fmaxf(v[idx], fmaf(acc[idx >> 4][idx & 15], a.scale_log2, neg_lse));
-          }
-        }
-#pragma unroll
-        for (int st = 0; st < D / 16; ++st) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);           // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 2 * kPer, 0);    // VALU
-        }
-        load_qfrag<D>(sm.qs, qb + 2 < ui.nqb ? qb + 2 : qb, qf);   // unconditional: one scheduling region
-        acc[0] = n0;
-        acc[1] = n1;
-      }
-      // Max over the 32 observation rows held by lanes l ^ {16,8,4,2,1}: each exchange
-      // halves the values a lane keeps, so lane l ends with value index (l & 31).
-#pragma unroll
-      for (int step = 16; step >= 1; step >>= 1) {
-        const bool upper = (lane & step) != 0;
-#pragma unroll
-        for (int i = 0; i < step; ++i) {
-          const float send = upper ? v[i] : v[i + step];
-          const float keep = upper ? v[i + step] : v[i];
-          v[i] = fmaxf(keep, __shfl_xor(send, step));
-        }
-      }
-      const int vi = lane & 31;
-      const int key = kbase + acc_key(vi >> 4, vi & 15, lane);
-      if (key < ui.L) sp[key] = ui.n_obs > 0 ? exp2f(v[0]) : 0.f;
+      float v = kNegInf;
+      if (ui.nqb > 0) v = finish_tile<D>(kf, sm.qs, sm.lse_s, ui.nqb, a.scale_log2);
+      const int key = kbase + lane;
+      if (key < ui.L) sp[key] = ui.n_obs > 0 ? exp2f(v) : 0.f;
     }
   }
-  __syncthreads();   // LDS is restaged by the next item
+  __syncthreads();   // LDS is restaged by the next segment
 }
 
-template <int D, int WAVES, bool FINISH>
-__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 8))) void score_kernel(const ScoreArgs a) {
+// ---- kernels ----------------------------------------------------------------------------
+
+template <int D, bool FINISH>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void score_kernel(const ScoreArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int n_items = a.units * a.splits;
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-    const int u = a.unit0 + item / a.splits;
-    const int split = item - (item / a.splits) * a.splits;
-    const UnitInfo ui = unit_info<WAVES>(a, u);
-    if (split >= ui.nsplits) continue;   // no keys in this split (uniform across the block)
-    if (FINISH)
-      pass2_item<D, WAVES>(a, u, split, ui, smem);
-    else
-      pass1_item<D, WAVES>(a, u, split, ui, smem);
+  const int w = static_cast<int>(blockIdx.x);
+  const int T = layer_tiles(a);
+  const long long N = static_cast<long long>(T) * a.n_layers;
+  // With fewer tiles than workgroups only the first N take part, so every share holds at
+  // least one tile and a unit's shares are consecutive workgroups.
+  const int G = static_cast<int>(N < gridDim.x ? N : gridDim.x);
+  if (w >= G) return;
+  const long long c0 = static_cast<long long>(w) * N / G;
+  const long long c1 = static_cast<long long>(w + 1) * N / G;
+  Cursor cur = locate(a, c0, T);
+  long long c = c0;
+  for (;;) {
+    const long long left = c1 - c;
+    const int n = static_cast<int>(left < cur.nt - cur.tile ? left : cur.nt - cur.tile);
+    const long long first = c - cur.tile;   // global index of the unit's first tile
+    const int w0 = owner(first, N, G);
+    const UnitInfo ui = unit_info(a, cur.u);
+    const size_t unit_part = static_cast<size_t>(cur.u) * a.slots * a.obs_pad;
+    if (FINISH) {
+      int n_part = owner(first + cur.nt - 1, N, G) - w0 + 1;
+      n_part = n_part < a.slots ? n_part : a.slots;
+      finish_segment<D>(a, ui, cur.tile, n, a.part_m + unit_part, a.part_z + unit_part, n_part, smem);
+    } else if (w - w0 < a.slots) {
+      const size_t o = unit_part + static_cast<size_t>(w - w0) * a.obs_pad;
+      stats_segment<D>(a, ui, cur.tile, n, a.part_m + o, a.part_z + o, smem);
+    }
+    c += n;
+    if (c >= c1 || !next_unit(a, cur)) break;
   }
 }
 
-template <int D, int WAVES>
-size_t lds_bytes(int obs_pad) {
-  return static_cast<size_t>(obs_pad) * (D * 2) + 4 * WAVES * obs_pad * sizeof(float);
+size_t lds_bytes(int head_dim, int obs_pad) {
+  return static_cast<size_t>(obs_pad) * (head_dim * 2) + 4 * kWaves * obs_pad * sizeof(float);
 }
 
-template <int D, int WAVES>
-hipError_t launch_d(ScoreArgs a, hipStream_t s) {
+template <int D>
+hipError_t launch_d(ScoreArgs a, int n_layers, hipStream_t s) {
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, [] {
-    attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&score_kernel<D, WAVES, false>),
+    attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&score_kernel<D, false>),
                                    hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (attr_err == hipSuccess)
-      attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&score_kernel<D, WAVES, true>),
+      attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&score_kernel<D, true>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   });
   if (attr_err != hipSuccess) return note_hip_error(attr_err, "score: hipFuncSetAttribute");
-  const size_t lds = lds_bytes<D, WAVES>(a.obs_pad);
+  const size_t lds = lds_bytes(D, a.obs_pad);
   int dev = 0, cus = 0, per_cu = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return note_hip_error(e, "score: hipGetDevice");
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return note_hip_error(e, "score: hipDeviceGetAttribute");
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, score_kernel<D, WAVES, true>, WAVES * 64, lds);
+  int per_cu_stats = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, score_kernel<D, true>, kThreads, lds);
   if (e != hipSuccess) return note_hip_error(e, "score: hipOccupancyMaxActiveBlocksPerMultiprocessor");
-  const int resident = std::max(1, per_cu) * cus;
-  a.tps = kScoreTilesPerItem;
-  a.splits = score_splits(a.capacity, a.obs_pad);
-  // One stats launch and one finish launch over every unit: the passes are bound by the
-  // matrix and vector units, not by memory (the finish pass re-reads the keys at a few
-  // TB/s), and every extra launch costs its ramp-up and tail.
-  const int total_units = a.units;
-  const int per_chunk = total_units;
-  for (int u0 = 0; u0 < total_units; u0 += per_chunk) {
-    a.unit0 = u0;
-    a.units = std::min(per_chunk, total_units - u0);
-    const int grid = std::min(resident, a.units * a.splits);
-    hipLaunchKernelGGL((score_kernel<D, WAVES, false>), dim3(grid), dim3(WAVES * 64), lds, s, a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return note_hip_error(e, "score: launch score_stats");
-    hipLaunchKernelGGL((score_kernel<D, WAVES, true>), dim3(grid), dim3(WAVES * 64), lds, s, a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return note_hip_error(e, "score: launch score_finish");
-  }
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_stats, score_kernel<D, false>, kThreads, lds);
+  if (e != hipSuccess) return note_hip_error(e, "score: hipOccupancyMaxActiveBlocksPerMultiprocessor");
+  // Every workgroup resident at once: the shares are equal, so none waits for a slot.
+  const int grid = std::min(kScoreMaxGrid, std::max(1, std::min(per_cu, per_cu_stats)) * cus);
+  a.n_layers = n_layers;
+  a.slots = score_slots(a.capacity, n_layers, a.n_kv_heads);
+  hipLaunchKernelGGL((score_kernel<D, false>), dim3(grid), dim3(kThreads), lds, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return note_hip_error(e, "score: launch score_stats");
+  hipLaunchKernelGGL((score_kernel<D, true>), dim3(grid), dim3(kThreads), lds, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return note_hip_error(e, "score: launch score_finish");
   return hipSuccess;
 }
 
 }  // namespace
 
-// Four waves per workgroup: the LDS (observation rows + per-wave statistics) is
-// obs_pad * (2D + 32) bytes, at most 160 KB, and up to 256 rows two workgroups share a CU.
-int score_waves(int /*obs_pad*/) { return 4; }
-
-hipError_t launch_score(const ScoreArgs& a, int /*n_layers*/, int head_dim, hipStream_t s) {
-  const int w = score_waves(a.obs_pad);
-  (void)w;
-  return head_dim == 128 ? launch_d<128, 4>(a, s) : launch_d<64, 4>(a, s);
+hipError_t launch_score(const ScoreArgs& a, int n_layers, int head_dim, hipStream_t s) {
+  if (head_dim == 128) return launch_d<128>(a, n_layers, s);
+  return launch_d<64>(a, n_layers, s);
 }
 
 }  // namespace bkv
