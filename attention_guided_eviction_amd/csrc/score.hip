@@ -204,6 +204,42 @@ __device__ inline void stage_queries(const ScoreArgs& a, const UnitInfo& ui, uin
 
 // ---- fragments --------------------------------------------------------------------------
 
+// Fragment s of observation rows blk*32 .. +31 from LDS: lane l holds row (l & 31), dims
+// 16*s + 8*(l >> 5) .. +7.  With the chunk swizzle the byte offset inside the row is
+// 16 * ((2s + half) ^ (row mod D/8)) = (32 s) ^ (16 * (half ^ (row mod D/8))), so each
+// fragment's address is one XOR away from a per-lane base.
+template <int D>
+__device__ inline bf16x8 q_frag(const uint8_t* qs, int blk, int s) {
+  const int lane = threadIdx.x & 63;
+  const int row = blk * 32 + (lane & 31);
+  const unsigned base = static_cast<unsigned>(row * (D * 2) + 16 * ((row & (D / 8 - 1)) ^ (lane >> 5)));
+  return *reinterpret_cast<const bf16x8*>(qs + (base ^ (32u * s)));
+}
+
+// Merge two (max, sum) pairs of exp2 statistics.
+__device__ inline void merge_stats(float& m, float& z, float m2, float z2) {
+  const float M = fmaxf(m, m2);
+  if (M == kNegInf) return;
+  z = z * __builtin_amdgcn_exp2f(m - M) + z2 * __builtin_amdgcn_exp2f(m2 - M);
+  m = M;
+}
+
+template <int D>
+struct Smem {
+  uint8_t* qs;   // [obs_pad][D] bf16, swizzled
+  float* st_m;   // [kWaves][2][obs_pad] (stats pass): per wave and lane half
+  float* st_z;   // [kWaves][2][obs_pad] (stats pass)
+  float* nlse;   // [obs_pad]            (finish pass; aliases st_m): -lse2_i / c
+  float* lse_s;
+  __device__ Smem(uint8_t* base, int obs_pad) {
+    qs = base;
+    st_m = reinterpret_cast<float*>(base + obs_pad * (D * 2));
+    st_z = st_m + 2 * kWaves * obs_pad;
+    nlse = st_m;
+    lse_s = st_m;
+  }
+};
+
 // Two 32-key fragments.  Lane l holds key (l & 31) of each fragment and, for k-step s,
 // dims 16*s + 8*(l >> 5) .. +7 (the A layout of keys in the stats pass and the B layout
 // in the finish pass are the same registers).  Keys past the valid length read row L-1
@@ -242,70 +278,89 @@ __device__ inline void load_qfrag(const uint8_t* qs, int qb, bf16x8 (&qf)[D / 16
     qf[s] = *reinterpret_cast<const bf16x8*>(base + (((2 * s + (lane >> 5)) ^ sw) * 16));
 }
 
-// Merge two (max, sum) pairs of exp2 statistics.
-__device__ inline void merge_stats(float& m, float& z, float m2, float z2) {
-  const float M = fmaxf(m, m2);
-  if (M == kNegInf) return;
-  z = z * __builtin_amdgcn_exp2f(m - M) + z2 * __builtin_amdgcn_exp2f(m2 - M);
-  m = M;
+// ---- key fragments ----------------------------------------------------------------------
+//
+// A wave takes the 64 keys it owns in a tile as two 32-key fragments, one after the other.
+// Three fragment buffers rotate: while fragment j is multiplied against every row block,
+// the loads of fragments j+1 and j+2 are in flight, so keys are requested two whole
+// fragment passes before their use and the bursts of reads from every wave at once have
+// time to drain.
+
+// One 32-key fragment: lane l holds key (l & 31) and, for k-step s, dims 16*s + 8*(l >> 5)
+// .. +7 (the A layout of keys in the stats pass and the B layout in the finish pass are
+// the same registers).  Keys past the valid length read row L-1 (in bounds) and are
+// masked or dropped by the caller.
+template <int D>
+struct Frag {
+  bf16x8 v[D / 16];
+};
+
+template <int D>
+__device__ inline void load_frag(const uint16_t* kp, int key0, int L, Frag<D>& f) {
+  const int lane = threadIdx.x & 63;
+  int key = key0 + (lane & 31);
+  key = key < L ? key : L - 1;
+  const uint16_t* src = kp + static_cast<size_t>(key) * D + (lane >> 5) * 8;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) f.v[s] = *reinterpret_cast<const bf16x8*>(src + s * 16);
+}
+
+// First key of fragment j of a segment that starts at tile tile0 and has nfrag fragments;
+// indices past the end give the last fragment again, so the loads stay unconditional.
+__device__ inline int frag_key(int tile0, int nfrag, int j) {
+  j = j < nfrag ? j : nfrag - 1;
+  return (tile0 + (j >> 1)) * kScoreTile + (threadIdx.x >> 6) * 64 + (j & 1) * 32;
 }
 
 template <int D>
-struct Smem {
-  uint8_t* qs;   // [obs_pad][D] bf16, swizzled
-  float* st_m;   // [kWaves][2][obs_pad] (stats pass): per wave and lane half
-  float* st_z;   // [kWaves][2][obs_pad] (stats pass)
-  float* lse_s;  // [obs_pad]            (finish pass; aliases st_m)
-  __device__ Smem(uint8_t* base, int obs_pad) {
-    qs = base;
-    st_m = reinterpret_cast<float*>(base + obs_pad * (D * 2));
-    st_z = st_m + 2 * kWaves * obs_pad;
-    lse_s = st_m;
+__device__ inline void pipeline_start(const uint16_t* kp, int L, int tile0, int nfrag, Frag<D> (&f)[3]) {
+#pragma unroll
+  for (int i = 0; i < 3; ++i) load_frag<D>(kp, frag_key(tile0, nfrag, i), L, f[i]);
+}
+
+// pass(frag, key0) for every fragment of the segment, in order.
+template <int D, class Pass>
+__device__ inline void pipeline_run(const uint16_t* kp, int L, int tile0, int nfrag, Frag<D> (&f)[3], Pass&& pass) {
+  for (int j = 0; j < nfrag; j += 3) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      if (j + i < nfrag) pass(f[i], frag_key(tile0, nfrag, j + i));
+      load_frag<D>(kp, frag_key(tile0, nfrag, j + i + 3), L, f[i]);
+    }
   }
-};
+}
 
 // ---- stats pass -------------------------------------------------------------------------
 
-// Key offset (within the wave's 64 keys) of accumulator r of fragment f in lane l, for the
-// stats layout (keys down the accumulator registers).
-__device__ inline int stats_key(int f, int r, int lane) {
-  return f * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+// Keys at or past L get -inf logits; accumulator r of lane l holds key
+// key0 + 8 (r >> 2) + 4 (l >> 5) + (r & 3) in the stats layout.
+__device__ inline void mask_frag(f32x16& acc, int key0, int L) {
+  const int half = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    if (key0 + 8 * (r >> 2) + 4 * half + (r & 3) >= L) acc[r] = kNegInf;
 }
 
-// Keys at or past L (only in a unit's last tile) get -inf logits.
-__device__ inline void mask_tail(f32x16 (&acc)[2], int kbase, int L, int lane) {
-#pragma unroll
-  for (int f = 0; f < 2; ++f)
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      if (kbase + stats_key(f, r, lane) >= L) acc[f][r] = kNegInf;
-}
-
-// Exact (max, sum) update of one lane's 32 logits of one row: the block max is taken and
+// Exact (max, sum) update of one lane's 16 logits of one row: the block max is taken and
 // the running sum rescaled.  Used for a row's first block and when the cheap update
 // reports a possible overflow.
-__device__ inline void row_update_exact(const f32x16 (&acc)[2], float c, float& m, float& z) {
+__device__ inline void row_update_exact(const f32x16& acc, float c, float& m, float& z) {
   float mx = kNegInf;
 #pragma unroll
-  for (int f = 0; f < 2; ++f)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[f][r]);
+  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[r]);
   if (mx == kNegInf) return;   // every key of this lane masked
   const float mt = fmaxf(mx * c, m);
   float zt = 0.f;
   const float neg = -mt;
 #pragma unroll
-  for (int f = 0; f < 2; ++f)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) zt += __builtin_amdgcn_exp2f(fmaf(acc[f][r], c, neg));
+  for (int r = 0; r < 16; ++r) zt += __builtin_amdgcn_exp2f(fmaf(acc[r], c, neg));
   z = (m == kNegInf ? 0.f : z * __builtin_amdgcn_exp2f(m - mt)) + zt;
   m = mt;
 }
 
 // With the running max m of earlier blocks the sum stays finite unless a logit exceeds
 // m by ~64 (it is +inf/NaN while m is still -inf); then the exact update redoes the block.
-__device__ inline void stats_commit(const f32x16 (&cur)[2], float zt, float c, float* pm, float* pz) {
-  float m = *pm, z = *pz;
+__device__ inline void stats_commit(const f32x16& cur, float zt, float c, float m, float z, float* pm, float* pz) {
   if (zt <= 1.8e19f)   // 2^64: no term overflowed (false for NaN and +inf)
     z += zt;
   else
@@ -314,81 +369,101 @@ __device__ inline void stats_commit(const f32x16 (&cur)[2], float zt, float c, f
   *pz = z;
 }
 
-// Sum of exp2(c * x - m) over the block in `cur` while the products of the next block
-// go into `nxt`; then rows nq*32.. are loaded into qf.
+// The block in `cur` (its rows' running statistics in m, z; their LDS copies at pm, pz)
+// is reduced to sums of exp2(c x - m) while the products of rows blk*32.. go into `nxt`.
+// qpre holds fragments 0 and 1 of block blk on entry and of block blk_next on exit (the
+// other fragments are read two MFMA steps ahead of their use); m, z hold the statistics
+// of the next block on exit.
 template <int D, bool MASK>
-__device__ inline void stats_step(const KeyFrag<D>& kf, bf16x8 (&qf)[D / 16], f32x16 (&cur)[2], f32x16 (&nxt)[2],
-                                  const uint8_t* qs, int nq, float c, float* pm, float* pz, int kbase, int L) {
-  const int lane = threadIdx.x & 63;
-  if (MASK) mask_tail(cur, kbase, L, lane);
-  const float neg = -*pm;
-  f32x16 n0 = {}, n1 = {};
+__device__ inline void stats_step(const Frag<D>& kf, bf16x8 (&qpre)[2], f32x16& cur, f32x16& nxt, const uint8_t* qs,
+                                  int blk, int blk_next, float c, float* pm, float* pz, float& m, float& z, int key0,
+                                  int L) {
+  constexpr int S = D / 16;
+  constexpr int kPer = 16 / S;   // logits handled per MFMA step
+  if (MASK) mask_frag(cur, key0, L);
+  const float m_next = pm[32], z_next = pz[32];
+  const float neg = -m;
+  f32x16 n = {};
   float zs[4] = {0.f, 0.f, 0.f, 0.f};
-  constexpr int kPer = 32 / (D / 16);   // logits handled per MFMA step
+  bf16x8 qf[S + 2];
+  qf[0] = qpre[0];
+  qf[1] = qpre[1];
 #pragma unroll
-  for (int st = 0; st < D / 16; ++st) {
-    n0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.v[0][st], qf[st], n0, 0, 0, 0);
-    n1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.v[1][st], qf[st], n1, 0, 0, 0);
+  for (int st = 0; st < S; ++st) {
+    qf[st + 2] = q_frag<D>(qs, st + 2 < S ? blk : blk_next, (st + 2) % S);
+    n = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.v[st], qf[st], n, 0, 0, 0);
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int idx = st * kPer + j;
-      zs[j & 3] += __builtin_amdgcn_exp2f(fmaf(cur[idx >> 4][idx & 15], c, neg));
+      zs[idx & 3] += __builtin_amdgcn_exp2f(fmaf(cur[idx], c, neg));
     }
   }
 #pragma unroll
-  for (int st = 0; st < D / 16; ++st) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);           // MFMA
+  for (int st = 0; st < S; ++st) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);           // LDS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // MFMA
     __builtin_amdgcn_sched_group_barrier(0x402, 3 * kPer, 0);    // VALU / transcendental
   }
-  load_qfrag<D>(qs, nq, qf);
-  stats_commit(cur, (zs[0] + zs[1]) + (zs[2] + zs[3]), c, pm, pz);
-  nxt[0] = n0;
-  nxt[1] = n1;
+  qpre[0] = qf[S];
+  qpre[1] = qf[S + 1];
+  stats_commit(cur, (zs[0] + zs[1]) + (zs[2] + zs[3]), c, m, z, pm, pz);
+  m = m_next;
+  z = z_next;
+  nxt = n;
 }
 
-// The last block of a tile: no products left to overlap.
+// The last block of a pass: no products left to overlap.
 template <bool MASK>
-__device__ inline void stats_last(f32x16 (&cur)[2], float c, float* pm, float* pz, int kbase, int L) {
-  const int lane = threadIdx.x & 63;
-  if (MASK) mask_tail(cur, kbase, L, lane);
-  const float neg = -*pm;
+__device__ inline void stats_last(f32x16& cur, float c, float* pm, float* pz, float m, float z, int key0, int L) {
+  if (MASK) mask_frag(cur, key0, L);
+  const float neg = -m;
   float zs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int idx = 0; idx < 32; ++idx) zs[idx & 3] += __builtin_amdgcn_exp2f(fmaf(cur[idx >> 4][idx & 15], c, neg));
-  stats_commit(cur, (zs[0] + zs[1]) + (zs[2] + zs[3]), c, pm, pz);
+  for (int r = 0; r < 16; ++r) zs[r & 3] += __builtin_amdgcn_exp2f(fmaf(cur[r], c, neg));
+  stats_commit(cur, (zs[0] + zs[1]) + (zs[2] + zs[3]), c, m, z, pm, pz);
 }
 
-// One wave's 64 keys against all nqb >= 1 row blocks.  pm/pz address the lane's
-// statistics of row block 0; block qb is at +qb*32.
+// One 32-key fragment (keys key0..) against all nqb >= 1 row blocks.  pm/pz address the
+// lane's statistics of row block 0; block qb is at +qb*32.
 template <int D, bool MASK>
-__device__ inline void stats_tile(const KeyFrag<D>& kf, const uint8_t* qs, int nqb, float c, float* pm, float* pz,
-                                  int kbase, int L) {
-  bf16x8 qf[D / 16];
-  f32x16 A[2], B[2];
-  load_qfrag<D>(qs, 0, qf);
+__device__ inline void stats_pass(const Frag<D>& kf, const uint8_t* qs, int nqb, float c, float* pm, float* pz,
+                                  int key0, int L) {
+  constexpr int S = D / 16;
+  f32x16 A, B;
   {
-    f32x16 c0 = {}, c1 = {};
+    bf16x8 q[S];
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.v[0][s], qf[s], c0, 0, 0, 0);
-      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.v[1][s], qf[s], c1, 0, 0, 0);
-    }
-    A[0] = c0;
-    A[1] = c1;
+    for (int s = 0; s < S; ++s) q[s] = q_frag<D>(qs, 0, s);
+    f32x16 acc = {};
+#pragma unroll
+    for (int s = 0; s < S; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.v[s], q[s], acc, 0, 0, 0);
+    A = acc;
   }
-  load_qfrag<D>(qs, nqb > 1 ? 1 : 0, qf);
+  const int b1 = nqb > 1 ? 1 : 0;
+  bf16x8 qpre[2] = {q_frag<D>(qs, b1, 0), q_frag<D>(qs, b1, 1)};
+  float m = pm[0], z = pz[0];
   int qb = 0;
   for (; qb + 2 < nqb; qb += 2) {
-    stats_step<D, MASK>(kf, qf, A, B, qs, qb + 2, c, pm + qb * 32, pz + qb * 32, kbase, L);
-    stats_step<D, MASK>(kf, qf, B, A, qs, qb + 3 < nqb ? qb + 3 : nqb - 1, c, pm + (qb + 1) * 32,
-                        pz + (qb + 1) * 32, kbase, L);
+    stats_step<D, MASK>(kf, qpre, A, B, qs, qb + 1, qb + 2, c, pm + qb * 32, pz + qb * 32, m, z, key0, L);
+    stats_step<D, MASK>(kf, qpre, B, A, qs, qb + 2, qb + 3 < nqb ? qb + 3 : nqb - 1, c, pm + (qb + 1) * 32,
+                        pz + (qb + 1) * 32, m, z, key0, L);
   }
   if (qb + 1 < nqb) {
-    stats_step<D, MASK>(kf, qf, A, B, qs, qb + 1, c, pm + qb * 32, pz + qb * 32, kbase, L);
-    stats_last<MASK>(B, c, pm + (qb + 1) * 32, pz + (qb + 1) * 32, kbase, L);
+    stats_step<D, MASK>(kf, qpre, A, B, qs, qb + 1, qb + 1, c, pm + qb * 32, pz + qb * 32, m, z, key0, L);
+    stats_last<MASK>(B, c, pm + (qb + 1) * 32, pz + (qb + 1) * 32, m, z, key0, L);
   } else {
-    stats_last<MASK>(A, c, pm + qb * 32, pz + qb * 32, kbase, L);
+    stats_last<MASK>(A, c, pm + qb * 32, pz + qb * 32, m, z, key0, L);
   }
+}
+
+template <int D>
+__device__ inline void stats_fragment(const Frag<D>& kf, const uint8_t* qs, int nqb, float c, float* pm, float* pz,
+                                      int key0, int L) {
+  if (key0 >= L || nqb == 0) return;
+  if (key0 + 32 <= L)
+    stats_pass<D, false>(kf, qs, nqb, c, pm, pz, key0, L);
+  else
+    stats_pass<D, true>(kf, qs, nqb, c, pm, pz, key0, L);
 }
 
 // Tiles tile0 .. tile0+ntile-1 of one unit -> partial statistics out_m/out_z [nqb*32].
@@ -399,31 +474,26 @@ __device__ void stats_segment(const ScoreArgs& a, const UnitInfo& ui, int tile0,
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const uint16_t* kp = a.k[ui.layer] + (static_cast<size_t>(ui.b) * a.n_kv_heads + ui.h) * a.capacity * D;
-  // No register prefetch of the next tile: two waves share each SIMD and a tile's work
-  // (several microseconds) covers the other wave's load latency, while 64 more
-  // registers per lane would force spills.
-  KeyFrag<D> kf;
-  load_keys<D>(kp, tile0 * kScoreTile + wave * 64, ui.L, kf);
+  Frag<D> fa, fb;
+  load_frag<D>(kp, tile0 * kScoreTile + (threadIdx.x >> 6) * 64, ui.L, fa);
+  load_frag<D>(kp, tile0 * kScoreTile + (threadIdx.x >> 6) * 64 + 32, ui.L, fb);
   stage_queries<D>(a, ui, sm.qs);
   for (int i = threadIdx.x; i < 2 * kWaves * a.obs_pad; i += kThreads) {
     sm.st_m[i] = kNegInf;
     sm.st_z[i] = 0.f;
   }
   const float c = a.scale_log2;
-  // lane (l & 31, l >> 5) keeps the statistics of row qb*32 + (l & 31) over its key half
   float* my_m = sm.st_m + (wave * 2 + (lane >> 5)) * a.obs_pad + (lane & 31);
   float* my_z = sm.st_z + (wave * 2 + (lane >> 5)) * a.obs_pad + (lane & 31);
   __syncthreads();
   const int t1 = tile0 + ntile;
   for (int t = tile0; t < t1; ++t) {
     const int kbase = t * kScoreTile + wave * 64;
-    if (t > tile0) load_keys<D>(kp, kbase, ui.L, kf);
-    if (kbase < ui.L && ui.nqb > 0) {
-      if (kbase + 64 <= ui.L)
-        stats_tile<D, false>(kf, sm.qs, ui.nqb, c, my_m, my_z, kbase, ui.L);
-      else
-        stats_tile<D, true>(kf, sm.qs, ui.nqb, c, my_m, my_z, kbase, ui.L);
-    }
+    const int knext = t + 1 < t1 ? kbase + kScoreTile : kbase;
+    stats_fragment<D>(fa, sm.qs, ui.nqb, c, my_m, my_z, kbase, ui.L);
+    load_frag<D>(kp, knext, ui.L, fa);
+    stats_fragment<D>(fb, sm.qs, ui.nqb, c, my_m, my_z, kbase + 32, ui.L);
+    load_frag<D>(kp, knext + 32, ui.L, fb);
   }
   __syncthreads();
   for (int i = threadIdx.x; i < ui.nqb * 32; i += kThreads) {

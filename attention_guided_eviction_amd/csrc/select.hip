@@ -1,12 +1,15 @@
 // Top-K selection under the cache budget with the recent window always kept
 // (BeaconKV page, Figure 5 (c)).
 //
-// One 1024-thread workgroup per unit.  The unit's scores (non-negative fp32, so their
-// bit patterns order like unsigned integers) sit in registers, element j in thread
-// j % 1024, slot j / 1024.  The k-th largest bit pattern T is found by a 32-step
-// bisection on the bits from the top (each step one block-wide count); every score
-// above T is kept and, of the scores equal to T, the lowest positions fill the rest.
-// Kept positions are written in ascending order by a ballot/prefix scan over the slots.
+// One 1024-thread workgroup per unit.  Thread t holds positions t*EPT .. t*EPT+EPT-1 of
+// the unit's scores in registers as bit patterns (non-negative fp32 order like unsigned
+// integers).  The k-th largest pattern T among the positions before the window is found
+// by a most-significant-digit-first radix select: four passes over 8-bit digits, each an
+// LDS histogram of the candidates that still match the digits chosen so far, scanned by
+// one wave.  Every score above T is kept and, of the scores equal to T, the lowest
+// positions fill the remaining slots; one block-wide scan of (ties, kept) counts in
+// position order gives every thread its tie rank and its output offset, so the kept
+// positions come out in ascending order.
 #include "bkv_internal.h"
 
 namespace bkv {
@@ -14,42 +17,65 @@ namespace {
 
 constexpr int kWaves = kSelectThreads / 64;
 
-// Block-wide sum of one int per thread.  `buf` holds kWaves ints; the caller alternates
-// two buffers between consecutive calls so a single barrier per call suffices.
-__device__ inline int block_sum(int x, int* buf) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) buf[wave] = x;
-  __syncthreads();
-  int s = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) s += buf[w];
-  return s;
-}
-
-// Exclusive prefix of `flag` over the block in thread order, plus the block total.
-__device__ inline int block_prefix(bool flag, int* buf, int& total) {
-  const unsigned long long m = __ballot(flag);
+// Exclusive prefix over the block (thread order) of a 64-bit value.  `buf` holds kWaves
+// entries; one barrier.
+__device__ inline unsigned long long block_exclusive_scan(unsigned long long x, unsigned long long* buf) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int in_wave = __popcll(m & ((1ull << lane) - 1ull));
-  if (lane == 0) buf[wave] = __popcll(m);
-  __syncthreads();
-  int before = 0, tot = 0;
+  unsigned long long incl = x;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const int c = buf[w];
-    before += w < wave ? c : 0;
-    tot += c;
+  for (int o = 1; o < 64; o <<= 1) {
+    const unsigned long long y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
   }
-  total = tot;
-  return before + in_wave;
+  if (lane == 63) buf[wave] = incl;
+  __syncthreads();
+  unsigned long long before = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) before += w < wave ? buf[w] : 0ull;
+  return before + incl - x;
+}
+
+// Wave 0: given the 256-bin histogram and the number r >= 1 of elements still to take
+// from the top, find the digit d with count(> d) < r <= count(>= d); store d and
+// r - count(> d) in out[0], out[1].  Clears the histogram for the next pass.
+__device__ inline void pick_digit(int* hist, int r, int* out) {
+  const int lane = threadIdx.x & 63;
+  const int4 h = *reinterpret_cast<const int4*>(hist + 4 * lane);   // bins 4l .. 4l+3
+  const int tot = h.x + h.y + h.z + h.w;
+  int suf = tot;   // inclusive suffix over lanes: bins >= 4l
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_down(suf, o);
+    if (lane + o < 64) suf += y;
+  }
+  const int above = suf - tot;   // bins >= 4l + 4
+  if (above < r && r <= suf) {
+    int d, gt;
+    if (above + h.w >= r) {
+      d = 4 * lane + 3;
+      gt = above;
+    } else if (above + h.w + h.z >= r) {
+      d = 4 * lane + 2;
+      gt = above + h.w;
+    } else if (above + h.w + h.z + h.y >= r) {
+      d = 4 * lane + 1;
+      gt = above + h.w + h.z;
+    } else {
+      d = 4 * lane;
+      gt = above + h.w + h.z + h.y;
+    }
+    out[0] = d;
+    out[1] = r - gt;
+  }
+  *reinterpret_cast<int4*>(hist + 4 * lane) = make_int4(0, 0, 0, 0);
 }
 
 template <int EPT>
 __global__ __launch_bounds__(kSelectThreads) void select_topk_kernel(const SelectArgs a) {
-  __shared__ int red[4][kWaves];
+  __shared__ __attribute__((aligned(16))) int hist[256];
+  __shared__ unsigned long long scan_buf[kWaves];
+  __shared__ int pick[2];
   const int u = blockIdx.x;
   const int per_layer = a.batch * a.n_kv_heads;
   const int layer = u / per_layer;
@@ -65,68 +91,91 @@ __global__ __launch_bounds__(kSelectThreads) void select_topk_kernel(const Selec
     if (tid == 0) a.n_kept[layer][bh] = L;
     return;
   }
-  const int prefix = L - a.window;
-  const int want = a.budget - a.window;  // slots filled from positions < prefix
+  const int prefix = L - a.window;       // candidates: positions < prefix
+  const int want = a.budget - a.window;  // slots filled from the candidates
   const float* sc = a.scores[layer] + static_cast<size_t>(bh) * a.capacity;
+  const int j0 = tid * EPT;
 
   uint32_t x[EPT];
+  if (EPT % 4 == 0 && (reinterpret_cast<uintptr_t>(sc) & 15) == 0 && j0 + EPT <= prefix) {
 #pragma unroll
-  for (int i = 0; i < EPT; ++i) {
-    const int j = tid + i * kSelectThreads;
-    x[i] = j < prefix ? __float_as_uint(sc[j]) : 0u;
+    for (int i = 0; i < EPT; i += 4) {
+      const uint4 v = *reinterpret_cast<const uint4*>(sc + j0 + i);
+      x[i] = v.x;
+      x[i + 1] = v.y;
+      x[i + 2] = v.z;
+      x[i + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) x[i] = j0 + i < prefix ? __float_as_uint(sc[j0 + i]) : 0u;
   }
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) x[i] = x[i] == 0x80000000u ? 0u : x[i];   // -0 orders as 0
 
-  // Largest T with count(x >= T) >= want, over positions < prefix.  Positions >= prefix
-  // hold 0 and are excluded from the count explicitly.
+  // Radix select of the want-th largest pattern among the candidates.
   uint32_t T = 0;
-  int buf = 0;
+  int need_eq = 0;   // ties at T to keep, lowest positions first
   if (want > 0) {
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = T | (1u << bit);
-      int c = 0;
+    if (tid < 64) *reinterpret_cast<int4*>(hist + 4 * tid) = make_int4(0, 0, 0, 0);
+    __syncthreads();
+    uint32_t P = 0;
+    int r = want;
 #pragma unroll
-      for (int i = 0; i < EPT; ++i) c += (tid + i * kSelectThreads < prefix && x[i] >= cand) ? 1 : 0;
-      if (block_sum(c, red[buf]) >= want) T = cand;
-      buf ^= 1;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) {
+        const bool match = j0 + i < prefix && (pass == 0 || (x[i] >> (shift + 8)) == P);
+        if (match) atomicAdd(&hist[(x[i] >> shift) & 255u], 1);
+      }
+      __syncthreads();
+      if (tid < 64) pick_digit(hist, r, pick);
+      __syncthreads();
+      P = (P << 8) | static_cast<uint32_t>(pick[0]);
+      r = pick[1];
     }
+    T = P;
+    need_eq = r;
   }
-  // Count the strictly larger ones and the ties at T.
-  int gt = 0, eq = 0;
-#pragma unroll
-  for (int i = 0; i < EPT; ++i) {
-    const bool v = tid + i * kSelectThreads < prefix;
-    gt += (v && x[i] > T) ? 1 : 0;
-    eq += (v && x[i] == T) ? 1 : 0;
-  }
-  const int n_gt = block_sum(gt, red[buf]);
-  buf ^= 1;
-  const int n_eq = block_sum(eq, red[buf]);
-  buf ^= 1;
-  const int need_eq = want > 0 ? want - n_gt : 0;   // ties at T to keep, lowest positions first
-  const bool all_eq = need_eq >= n_eq;
 
-  int eq_base = 0, sel_base = 0;
+  // Per-thread counts in position order: ties at T, and positions kept outright
+  // (candidates above T, and the window).
+  int n_eq = 0, n_fixed = 0;
 #pragma unroll
   for (int i = 0; i < EPT; ++i) {
-    const int j = tid + i * kSelectThreads;
-    if (i * kSelectThreads >= L) break;   // uniform across the block
-    const bool v = j < prefix;
-    const bool is_eq = want > 0 && v && x[i] == T;
-    bool keep = (want > 0 && v && x[i] > T) || (j >= prefix && j < L);
-    if (all_eq) {
-      keep = keep || is_eq;
-    } else {
-      int tot;
-      const int rank = eq_base + block_prefix(is_eq, red[buf], tot);
-      buf ^= 1;
-      eq_base += tot;
-      keep = keep || (is_eq && rank < need_eq);
+    const int j = j0 + i;
+    if (j < prefix) {
+      if (want > 0) {
+        n_fixed += x[i] > T ? 1 : 0;
+        n_eq += x[i] == T ? 1 : 0;
+      }
+    } else if (j < L) {
+      ++n_fixed;
     }
-    int tot;
-    const int pos = sel_base + block_prefix(keep, red[buf], tot);
-    buf ^= 1;
-    sel_base += tot;
-    if (keep && pos < a.budget) out[pos] = j;
+  }
+  const unsigned long long before =
+      block_exclusive_scan((static_cast<unsigned long long>(n_eq) << 32) | static_cast<unsigned>(n_fixed), scan_buf);
+  int eq_seen = static_cast<int>(before >> 32);
+  const int fixed_before = static_cast<int>(before & 0xffffffffu);
+  int pos = fixed_before + (eq_seen < need_eq ? eq_seen : need_eq);
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    const int j = j0 + i;
+    bool keep;
+    if (j < prefix) {
+      keep = want > 0 && x[i] > T;
+      if (want > 0 && x[i] == T) {
+        keep = eq_seen < need_eq;
+        ++eq_seen;
+      }
+    } else {
+      keep = j < L;
+    }
+    if (keep) {
+      if (pos < a.budget) out[pos] = j;
+      ++pos;
+    }
   }
   if (tid == 0) a.n_kept[layer][bh] = a.budget;
 }
