@@ -36,7 +36,11 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="qwen7b_16k")
     p.add_argument("--cpu-units", type=int, default=-1,
-                   help="units in the CPU-oracle sample (0: skip; -1: every unit if at most 160, else 64)")
+                   help="at most this many units in the CPU-oracle sample (0: skip; -1: no limit; "
+                        "the sample stops after about 15 s of oracle time either way)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a plain 1 GiB device copy five times (a known-size reference for the "
+                            "FETCH_SIZE / WRITE_SIZE counters)")
     p.add_argument("--quiet", action="store_true")
     return p.parse_args()
 
@@ -66,24 +70,46 @@ def score_flops(w, lens):
     return sum(2.0 * n_obs * int(L) * w.head_dim * w.n_layers * w.n_kv_heads for L in lens)
 
 
-def cpu_baseline(w, n_units):
-    """Time the CPU oracle on a bounded sample of units of the same workload."""
+def score_traffic(workload):
+    """HBM bytes per bkv_score call from the committed counter summary for this workload,
+    or None when there is none or the scorer source has changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"score_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.lstrip().startswith("#"):
+                k, v = line.split("=", 1)
+                vals[k.strip()] = v.strip()
+    src = os.path.join(ROOT, "attention_guided_eviction_amd", "csrc", "score.hip")
+    with open(src, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    if vals.get("score_hip_sha256") != digest or "traffic_bytes_per_call" not in vals:
+        return None
+    return float(vals["traffic_bytes_per_call"])
+
+
+def cpu_baseline(w, n_units, budget_s=15.0):
+    """Time the CPU oracle on a bounded sample of units of the same workload: units in a
+    seeded random order until about budget_s seconds of oracle time or n_units units
+    (-1: no unit limit)."""
     import numpy as np
     import threadpoolctl
-    from synth import unit_inputs, bf16_bits, seq_lengths
+    from synth import unit_inputs, bf16_bits
     from oracle import bkv_oracle as O
     rng = np.random.default_rng(1)
-    if n_units < 0:
-        n_units = w.units if w.units <= 160 else 64
-    if n_units >= w.units:
-        units = [(l, b, h) for l in range(w.n_layers) for b in range(w.batch) for h in range(w.n_kv_heads)]
-        n_units = len(units)
-    else:
-        units = [(int(rng.integers(w.n_layers)), int(rng.integers(w.batch)), int(rng.integers(w.n_kv_heads)))
-                 for _ in range(n_units)]
+    order = rng.permutation(w.units)
+    if n_units > 0:
+        order = order[:n_units]
     t_total = 0.0
     keys_total = 0
-    for (l, b, h) in units:
+    done = 0
+    per_layer = w.batch * w.n_kv_heads
+    for u_id in order:
+        l, rem = divmod(int(u_id), per_layer)
+        b, h = divmod(rem, w.n_kv_heads)
         u = unit_inputs(w, l, b, h, "cpu")
         kb, vb, qb, bb = bf16_bits(u["k"]), bf16_bits(u["v"]), bf16_bits(u["q"]), bf16_bits(u["beacons"])
         t0 = time.perf_counter()
@@ -93,15 +119,18 @@ def cpu_baseline(w, n_units):
         O.compress_unit(kb, vb, qb, bb, nb, w.window, w.budget)
         t_total += time.perf_counter() - t0
         keys_total += u["L"]
+        done += 1
+        if t_total >= budget_s:
+            break
     # tokens/s: a token is compressed once all layers x KV heads of its sequence are done
     rows_per_s = keys_total / t_total
     tokens_per_s = rows_per_s / (w.n_layers * w.n_kv_heads)
     info = threadpoolctl.threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info] or [1])
     return {"value": tokens_per_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n_units} (layer, sequence, KV head) units of {w.name}, "
-                      f"{keys_total} cached rows, {t_total:.1f} s of float64 NumPy "
-                      f"(beacon update, scores, top-K, compaction); scaled by layers x KV heads"}
+            "sample": f"{done} of {w.units} (layer, sequence, KV head) units of {w.name} in seeded random order "
+                      f"(stop after ~{budget_s:.0f} s), {keys_total} cached rows, {t_total:.1f} s of float64 NumPy "
+                      f"(beacon update, scores, top-K, compaction); rows/s divided by layers x KV heads"}
 
 
 def main():
@@ -174,12 +203,14 @@ def main():
     total_bytes = sum(ab.values())
     dom = max(per, key=per.get)
     achieved = ab[dom] / (per[dom] * 1e-3) / 1e9
-    roof = {"kernel": {"score": "score_pass1 + score_merge + score_pass2 (bkv_score)",
+    traffic = score_traffic(w.name) if dom == "score" else None
+    roof = {"kernel": {"score": "score_kernel<D,false> (stats) + score_kernel<D,true> (finish): one bkv_score call",
                        "select": "select_topk_kernel (bkv_select_topk)",
                        "compact": "compact_kernel (bkv_compact)",
                        "update_beacons": "fps_kernel (bkv_update_beacons)"}[dom],
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None if traffic is None else round(traffic),
             "ms_per_launch": round(per[dom], 4), "alg_bytes_per_launch": ab[dom]}
     if dom == "score":
         tf = score_flops(w, lens) / (per[dom] * 1e-3) / 1e12
@@ -201,6 +232,14 @@ def main():
         "per_call_ms": {n: round(t, 4) for n, t in per.items()},
         "roofline": roof,
     }
+    if args.copy_calibration:
+        n = 1 << 28   # 1 GiB of float32
+        src = torch.ones(n, device=dev)
+        dst = torch.empty(n, device=dev)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if args.cpu_units != 0:
         log("[bench] CPU oracle on a sample ...")
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_units)
