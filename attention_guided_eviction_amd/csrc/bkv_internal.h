@@ -68,7 +68,7 @@ struct CompactArgs {
 };
 
 // ---- beacons -----------------------------------------------------------------------------
-constexpr int kFpsThreads = 512;
+constexpr int kFpsThreads = 1024;   // one pool row per thread: pools up to 1024 rows
 
 struct FpsArgs {
   const uint16_t* beacons_in[kMaxLayers];

@@ -3,12 +3,14 @@
 // global query clusters without keeping the query history; Figure 4 (a): cosine
 // similarity between queries).
 //
-// One 512-thread workgroup per unit.  The pool (live beacons, then the group's new
-// queries head-major in time order) is held in registers: a row is spread over D/8
-// lanes, 16 bytes (8 bf16) each, and group g of D/8 lanes owns rows g, g + G, g + 2G...
-// (G = 512 / (D/8) groups).  Each pick broadcasts the chosen row through LDS, every
-// group updates the distance of its rows to their nearest chosen row, and a block-wide
-// argmax (largest distance, lowest pool index on ties) names the next pick.
+// One workgroup per unit, one thread per pool row (the workgroup is the largest pool
+// rounded up to whole waves, so two units share a CU on the largest workloads); thread p
+// holds pool row p (live beacons, then the group's new queries head-major in time order)
+// in registers as packed bf16 pairs, with its inverse norm.  A pick is uniform across the workgroup, so every wave reads the
+// picked row straight from its (read-only) source through scalar loads and each thread
+// takes the dot product of its row with it by v_dot2_f32_bf16 with the row in SGPRs: no
+// cross-lane reduction per row.  Each thread keeps its row's distance to the nearest
+// chosen row; a block-wide max of (distance, lowest index on ties) names the next pick.
 #include "bkv_internal.h"
 
 namespace bkv {
@@ -17,32 +19,33 @@ namespace {
 constexpr int kWaves = kFpsThreads / 64;
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef const __attribute__((address_space(4))) uint32_t* const_u32;
 
-// Dot product of 8 bf16 pairs with fp32 accumulation (v_dot2_f32_bf16 consumes the
-// packed pairs directly, so rows stay packed in registers).
-__device__ inline float dot8(const uint4& x, const uint4& y) {
-  float s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x.x), __builtin_bit_cast(bf16x2, y.x), 0.f, false);
-  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x.y), __builtin_bit_cast(bf16x2, y.y), s, false);
-  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x.z), __builtin_bit_cast(bf16x2, y.z), s, false);
-  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x.w), __builtin_bit_cast(bf16x2, y.w), s, false);
-  return s;
+__device__ inline float dot2(uint32_t x, uint32_t y, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), __builtin_bit_cast(bf16x2, y), acc, false);
 }
 
-template <int LPR>
-__device__ inline float group_sum(float v) {
-#pragma unroll
-  for (int o = LPR / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+// Max over the wave of non-negative 32-bit values: four DPP steps give every lane its
+// 16-lane row's max (lane pairs i^1, i^2, then mirrors within 8 and 16 lanes), and the
+// four rows meet in scalar registers.
+__device__ inline unsigned wave_umax(unsigned v) {
+  v = max(v, static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0xB1, 0xF, 0xF, false)));   // quad_perm 1,0,3,2
+  v = max(v, static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x4E, 0xF, 0xF, false)));   // quad_perm 2,3,0,1
+  v = max(v, static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x141, 0xF, 0xF, false)));  // row_half_mirror
+  v = max(v, static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x140, 0xF, 0xF, false)));  // row_mirror
+  const unsigned r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+  const unsigned r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+  return max(max(r0, r1), max(r2, r3));
 }
 
-template <int D, int RPG>
+template <int D>
 __global__ __launch_bounds__(kFpsThreads) void fps_kernel(const FpsArgs a) {
-  constexpr int LPR = D / 8;
-  constexpr int GROUPS = kFpsThreads / LPR;
-  __shared__ uint4 pick_row[LPR];
-  __shared__ float pick_inv;
-  __shared__ float wbest_v[kWaves];
-  __shared__ int wbest_i[kWaves];
+  constexpr int W = D / 2;   // 32-bit words (bf16 pairs) per row
+  __shared__ float inv_s[kFpsThreads];
+  __shared__ unsigned best_v[2][kWaves];
+  __shared__ int best_i[2][kWaves];
+  const int nthr = static_cast<int>(blockDim.x);
+  const int nwaves = nthr >> 6;
 
   const int u = blockIdx.x;
   const int per_layer = a.batch * a.n_kv_heads;
@@ -67,9 +70,10 @@ __global__ __launch_bounds__(kFpsThreads) void fps_kernel(const FpsArgs a) {
   };
 
   if (P <= a.nb_max) {  // everything fits: keep the pool as is
-    for (int e = tid; e < P * LPR; e += kFpsThreads) {
-      const int p = e / LPR;
-      const int cc = e - p * LPR;
+    constexpr int kChunks = D / 8;
+    for (int e = tid; e < P * kChunks; e += nthr) {
+      const int p = e / kChunks;
+      const int cc = e - p * kChunks;
       *reinterpret_cast<uint4*>(out + static_cast<size_t>(p) * D + cc * 8) =
           *reinterpret_cast<const uint4*>(row_ptr(p) + cc * 8);
     }
@@ -77,79 +81,71 @@ __global__ __launch_bounds__(kFpsThreads) void fps_kernel(const FpsArgs a) {
     return;
   }
 
-  const int g = tid / LPR;
-  const int c = tid - g * LPR;
-  uint4 xr[RPG];
-  float inv[RPG];
-  float mind[RPG];
-  uint32_t taken = 0;  // bit k: row k*GROUPS+g already chosen (or absent)
+  const int p = tid;
+  const bool have = p < P;
+  uint32_t x[W];
+  if (have) {
+    const uint4* src = reinterpret_cast<const uint4*>(row_ptr(p));
 #pragma unroll
-  for (int k = 0; k < RPG; ++k) {
-    const int p = k * GROUPS + g;
-    xr[k] = p < P ? *reinterpret_cast<const uint4*>(row_ptr(p) + c * 8) : make_uint4(0, 0, 0, 0);
-    const float ss = group_sum<LPR>(dot8(xr[k], xr[k]));
-    inv[k] = 1.0f / fmaxf(sqrtf(ss), 1e-30f);
-    mind[k] = 0.f;
-    if (p >= P) taken |= 1u << k;
+    for (int i = 0; i < W / 4; ++i) {
+      const uint4 v = src[i];
+      x[4 * i] = v.x;
+      x[4 * i + 1] = v.y;
+      x[4 * i + 2] = v.z;
+      x[4 * i + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < W; ++i) x[i] = 0u;
   }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < W; ++i) ss = dot2(x[i], x[i], ss);
+  const float inv = 1.0f / fmaxf(sqrtf(ss), 1e-30f);
+  inv_s[tid] = inv;
+  __syncthreads();   // every row's inverse norm is read by index below
 
+  float mind = 0.f;
+  bool avail = have;
   int cur = 0;
   for (int t = 0; t < a.nb_max; ++t) {
-    if (g == cur % GROUPS) {
-      const int k0 = cur / GROUPS;
+    if (p == cur) {   // the pick's owner writes it out and leaves the candidates
+      uint4* dst = reinterpret_cast<uint4*>(out + static_cast<size_t>(t) * D);
 #pragma unroll
-      for (int k = 0; k < RPG; ++k)
-        if (k == k0) {
-          pick_row[c] = xr[k];
-          *reinterpret_cast<uint4*>(out + static_cast<size_t>(t) * D + c * 8) = xr[k];
-          if (c == 0) pick_inv = inv[k];
-          taken |= 1u << k;
-        }
+      for (int i = 0; i < W / 4; ++i) dst[i] = make_uint4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
+      avail = false;
     }
-    __syncthreads();
     if (t == a.nb_max - 1) break;
-    const uint4 y = pick_row[c];
-    const float ip = pick_inv;
-    float best_v = -1.f;
-    int best_i = 0x7FFFFFFF;
+    unsigned key = 0;   // distance bits + 1 (monotone for distances >= 0); 0: cannot be picked
+    if ((tid & ~63) < P) {   // waves holding no pool row skip the products
+      const const_u32 y = (const_u32)(row_ptr(cur));   // uniform: scalar loads
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};   // four chains: shorter dependency
 #pragma unroll
-    for (int k = 0; k < RPG; ++k) {
-      const float dt = group_sum<LPR>(dot8(xr[k], y));
-      float d = 1.0f - dt * inv[k] * ip;
+      for (int i = 0; i < W; ++i) acc[i & 3] = dot2(x[i], y[i], acc[i & 3]);
+      const float dt = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+      float d = 1.0f - dt * inv * inv_s[cur];
       d = fminf(fmaxf(d, 0.f), 2.f);
-      mind[k] = t == 0 ? d : fminf(mind[k], d);
-      const float v = (taken >> k) & 1u ? -1.f : mind[k];
-      if (v > best_v) {  // k ascending = pool index ascending: strict > keeps the lowest
-        best_v = v;
-        best_i = k * GROUPS + g;
-      }
+      mind = t == 0 ? d : fminf(mind, d);
+      key = avail ? __float_as_uint(mind) + 1u : 0u;
     }
-#pragma unroll
-    for (int o = LPR; o < 64; o <<= 1) {
-      const float ov = __shfl_xor(best_v, o);
-      const int oi = __shfl_xor(best_i, o);
-      if (ov > best_v || (ov == best_v && oi < best_i)) {
-        best_v = ov;
-        best_i = oi;
-      }
-    }
+    const unsigned wmax = wave_umax(key);
+    // lowest lane holding the wave max = lowest pool index of the wave
+    const unsigned long long hit = __ballot(key == wmax);
     if ((tid & 63) == 0) {
-      wbest_v[tid >> 6] = best_v;
-      wbest_i[tid >> 6] = best_i;
+      best_v[t & 1][tid >> 6] = wmax;
+      best_i[t & 1][tid >> 6] = (tid & ~63) + __ffsll(static_cast<long long>(hit)) - 1;
     }
     __syncthreads();
-    best_v = wbest_v[0];
-    best_i = wbest_i[0];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) {
-      const float ov = wbest_v[w];
-      const int oi = wbest_i[w];
-      if (ov > best_v || (ov == best_v && oi < best_i)) {
-        best_v = ov;
-        best_i = oi;
+    unsigned bv = best_v[t & 1][0];
+    int bi = best_i[t & 1][0];
+    for (int w = 1; w < nwaves; ++w) {   // waves in index order: strict > keeps the lowest
+      const unsigned ov = best_v[t & 1][w];
+      if (ov > bv) {
+        bv = ov;
+        bi = best_i[t & 1][w];
       }
     }
-    cur = best_i;
+    cur = __builtin_amdgcn_readfirstlane(bi);
   }
   if (tid == 0) a.n_out[layer][bh] = a.nb_max;
 }
@@ -157,27 +153,14 @@ __global__ __launch_bounds__(kFpsThreads) void fps_kernel(const FpsArgs a) {
 }  // namespace
 
 hipError_t launch_fps(const FpsArgs& a, int n_layers, int head_dim, int pool_max, hipStream_t s) {
+  if (pool_max > kFpsThreads) return hipErrorInvalidValue;   // rejected by the host beforehand
   const unsigned grid = static_cast<unsigned>(n_layers) * a.batch * a.n_kv_heads;
-  const int groups = kFpsThreads / (head_dim / 8);
-  const int rpg = (pool_max + groups - 1) / groups;
-#define BKV_FPS_CASE(R)                                                                   \
-  if (rpg <= R) {                                                                         \
-    if (head_dim == 128)                                                                  \
-      hipLaunchKernelGGL((fps_kernel<128, R>), dim3(grid), dim3(kFpsThreads), 0, s, a);  \
-    else                                                                                  \
-      hipLaunchKernelGGL((fps_kernel<64, R>), dim3(grid), dim3(kFpsThreads), 0, s, a);   \
-    return note_hip_error(hipGetLastError(), "fps: launch");                                                             \
-  }
-  BKV_FPS_CASE(1)
-  BKV_FPS_CASE(2)
-  BKV_FPS_CASE(4)
-  BKV_FPS_CASE(8)
-  BKV_FPS_CASE(12)
-  BKV_FPS_CASE(16)
-  BKV_FPS_CASE(20)
-  BKV_FPS_CASE(24)
-#undef BKV_FPS_CASE
-  return hipErrorInvalidValue;  // pool above BKV_MAX_POOL: rejected by the host beforehand
+  const int threads = pool_max < 64 ? 64 : (pool_max + 63) / 64 * 64;
+  if (head_dim == 128)
+    hipLaunchKernelGGL(fps_kernel<128>, dim3(grid), dim3(threads), 0, s, a);
+  else
+    hipLaunchKernelGGL(fps_kernel<64>, dim3(grid), dim3(threads), 0, s, a);
+  return note_hip_error(hipGetLastError(), "fps: launch");
 }
 
 }  // namespace bkv
