@@ -34,14 +34,16 @@ struct ScoreArgs {
   int q_len, window, nb_max;
   int obs_pad;          // observation rows per unit rounded up to 32 (launch-wide)
   int slots;            // statistics slots per unit (set by the launcher)
+  int paired;           // two workgroups per CU, w and w + grid/2 (set by the launcher)
   float scale_log2;     // log2(e) / sqrt(head_dim)
 };
 
 // Statistics slots per unit for a launch of n_layers layers (the workspace is sized from
-// this): one per workgroup that can share a unit, never more than the unit's tiles.
+// this): one per workgroup that can share a unit (the smallest share is at least 4/5 of
+// the mean), never more than the unit's tiles.
 inline int score_slots(int capacity, int n_layers, int n_kv_heads) {
   const int tiles = (capacity + kScoreTile - 1) / kScoreTile;
-  const int sharing = kScoreMaxGrid / (n_layers * n_kv_heads) + 2;
+  const int sharing = kScoreMaxGrid * 5 / 4 / (n_layers * n_kv_heads) + 2;   // share weights up to 3:2
   return tiles < sharing ? tiles : sharing;
 }
 

@@ -128,10 +128,25 @@ __device__ inline bool next_unit(const ScoreArgs& a, Cursor& cur) {
   return false;
 }
 
-// Workgroup whose share holds global tile c.
-__device__ inline int owner(long long c, long long N, int G) {
-  return static_cast<int>(((c + 1) * G + N - 1) / N - 1);
-}
+// The launch's split of N tiles over G workgroups.  Workgroups w and w + G/2 share a CU
+// (two per CU, dispatched in index order), and the SIMDs' arbiters favour the older waves,
+// so the first half runs faster while both are resident: shares are weighted A : B
+// between the halves so that both finish together.  cum(w) is the weight of
+// workgroups 0 .. w-1; workgroup w owns tiles [cum(w) N / cum(G), cum(w+1) N / cum(G)).
+struct Split {
+  long long N;
+  int G, H, A, B;
+  __device__ long long cum(int w) const {
+    return w <= H ? static_cast<long long>(A) * w : static_cast<long long>(A) * H + static_cast<long long>(B) * (w - H);
+  }
+  __device__ long long begin(int w) const { return cum(w) * N / cum(G); }
+  // Workgroup whose share holds global tile c: the last w with begin(w) <= c.
+  __device__ int owner(long long c) const {
+    const long long x = ((c + 1) * cum(G) + N - 1) / N - 1;   // largest cum(w) allowed
+    const long long w = x < static_cast<long long>(A) * H ? x / A : H + (x - static_cast<long long>(A) * H) / B;
+    return static_cast<int>(w < G - 1 ? w : G - 1);
+  }
+};
 
 
 // ---- per-unit data ------------------------------------------------------------------------
@@ -660,29 +675,45 @@ __device__ void finish_segment(const ScoreArgs& a, const UnitInfo& ui, int tile0
 
 // ---- kernels ----------------------------------------------------------------------------
 
+// Share weights of the older : newer workgroup of each CU, measured on MI355X (older
+// workgroups finished the stats pass in 126 us against 153 us, the finish pass in 103 us
+// against 117 us, with equal shares).
+constexpr int kStatsWeightOld = 9, kStatsWeightNew = 7;
+constexpr int kFinishWeightOld = 15, kFinishWeightNew = 13;
+
 template <int D, bool FINISH>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void score_kernel(const ScoreArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int w = static_cast<int>(blockIdx.x);
   const int T = layer_tiles(a);
-  const long long N = static_cast<long long>(T) * a.n_layers;
+  Split sp;
+  sp.N = static_cast<long long>(T) * a.n_layers;
   // With fewer tiles than workgroups only the first N take part, so every share holds at
   // least one tile and a unit's shares are consecutive workgroups.
-  const int G = static_cast<int>(N < gridDim.x ? N : gridDim.x);
-  if (w >= G) return;
-  const long long c0 = static_cast<long long>(w) * N / G;
-  const long long c1 = static_cast<long long>(w + 1) * N / G;
+  sp.G = static_cast<int>(sp.N < gridDim.x ? sp.N : gridDim.x);
+  if (w >= sp.G) return;
+  // Weighted shares only where the pairs are real and every share keeps two tiles or more.
+  const bool weighted = a.paired && sp.G == static_cast<int>(gridDim.x) && (sp.G & 1) == 0 && sp.N >= 2LL * sp.G;
+  sp.H = sp.G / 2;
+  // Partial slots are numbered by the stats pass's split in both passes.
+  Split ss = sp;
+  ss.A = weighted ? kStatsWeightOld : 1;
+  ss.B = weighted ? kStatsWeightNew : 1;
+  sp.A = weighted ? (FINISH ? kFinishWeightOld : kStatsWeightOld) : 1;
+  sp.B = weighted ? (FINISH ? kFinishWeightNew : kStatsWeightNew) : 1;
+  const long long c0 = sp.begin(w);
+  const long long c1 = sp.begin(w + 1);
   Cursor cur = locate(a, c0, T);
   long long c = c0;
   for (;;) {
     const long long left = c1 - c;
     const int n = static_cast<int>(left < cur.nt - cur.tile ? left : cur.nt - cur.tile);
     const long long first = c - cur.tile;   // global index of the unit's first tile
-    const int w0 = owner(first, N, G);
+    const int w0 = ss.owner(first);   // slot 0 of the unit's partials
     const UnitInfo ui = unit_info(a, cur.u);
     const size_t unit_part = static_cast<size_t>(cur.u) * a.slots * a.obs_pad;
     if (FINISH) {
-      int n_part = owner(first + cur.nt - 1, N, G) - w0 + 1;
+      int n_part = ss.owner(first + cur.nt - 1) - w0 + 1;
       n_part = n_part < a.slots ? n_part : a.slots;
       finish_segment<D>(a, ui, cur.tile, n, a.part_m + unit_part, a.part_z + unit_part, n_part, smem);
     } else if (w - w0 < a.slots) {
@@ -725,6 +756,7 @@ hipError_t launch_d(ScoreArgs a, int n_layers, hipStream_t s) {
   const int grid = std::min(kScoreMaxGrid, std::max(1, std::min(per_cu, per_cu_stats)) * cus);
   a.n_layers = n_layers;
   a.slots = score_slots(a.capacity, n_layers, a.n_kv_heads);
+  a.paired = std::min(per_cu, per_cu_stats) == 2 ? 1 : 0;
   hipLaunchKernelGGL((score_kernel<D, false>), dim3(grid), dim3(kThreads), lds, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return note_hip_error(e, "score: launch score_stats");
