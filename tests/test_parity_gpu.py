@@ -48,6 +48,12 @@ EDGE = {
     # largest observation set: 4 * 120 + 32 = 512 rows
     "max_obs": WORKLOADS["qwen7b_16k"].replace(n_layers=1, n_q_heads=16, n_kv_heads=4, window=120, nb_init=32,
                                                nb_max=32, capacity=1500, seq_len=1500, budget=600),
+    # head_dim 64 with 6 row blocks: two blocks on some waves of the register-resident stats pass
+    "two_blocks_d64": WORKLOADS["tiny"].replace(n_q_heads=16, n_kv_heads=2, window=20, nb_init=16, nb_max=16,
+                                                t_new=0, capacity=900, seq_len=877, budget=300),
+    # exactly 256 observation rows (7 * 32 + 32), the most the register-resident stats pass takes
+    "obs_256": WORKLOADS["qwen7b_16k"].replace(n_layers=1, capacity=1300, seq_len=1291, budget=400, nb_init=32,
+                                               nb_max=32),
     # window equals budget: nothing chosen by score
     "window_eq_budget": WORKLOADS["tiny"].replace(window=8, budget=8, t_new=0, capacity=400, seq_len=400),
     # more layers than one launch holds (48)
