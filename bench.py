@@ -70,10 +70,43 @@ def score_flops(w, lens):
     return sum(2.0 * n_obs * int(L) * w.head_dim * w.n_layers * w.n_kv_heads for L in lens)
 
 
+SCORER_SOURCES = ("score.hip", "score_qs.hip", "score_common.h")
+
+
+def scorer_digest():
+    """sha256 over the scorer's sources, in a fixed order."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in SCORER_SOURCES:
+        with open(os.path.join(ROOT, "attention_guided_eviction_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def copy_ceiling(dev, gib=2, reps=5):
+    """Read+write copy rate of a plain device copy of `gib` GiB (2*gib GiB moved), median of reps."""
+    import statistics
+    import torch
+    n = gib << 28   # float32 elements
+    src = torch.ones(n, device=dev)
+    dst = torch.empty(n, device=dev)
+    dst.copy_(src)
+    times = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * gib * (1 << 30) / (statistics.median(times) * 1e-3) / 1e9
+
+
 def score_traffic(workload):
     """HBM bytes per bkv_score call from the committed counter summary for this workload,
     or None when there is none or the scorer source has changed since it was taken."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", f"score_traffic_{workload}.txt")
     if not os.path.exists(path):
         return None
@@ -83,10 +116,7 @@ def score_traffic(workload):
             if "=" in line and not line.lstrip().startswith("#"):
                 k, v = line.split("=", 1)
                 vals[k.strip()] = v.strip()
-    src = os.path.join(ROOT, "attention_guided_eviction_amd", "csrc", "score.hip")
-    with open(src, "rb") as f:
-        digest = hashlib.sha256(f.read()).hexdigest()
-    if vals.get("score_hip_sha256") != digest or "traffic_bytes_per_call" not in vals:
+    if vals.get("scorer_sha256") != scorer_digest() or "traffic_bytes_per_call" not in vals:
         return None
     return float(vals["traffic_bytes_per_call"])
 
@@ -204,7 +234,8 @@ def main():
     dom = max(per, key=per.get)
     achieved = ab[dom] / (per[dom] * 1e-3) / 1e9
     traffic = score_traffic(w.name) if dom == "score" else None
-    roof = {"kernel": {"score": "score_kernel<D,false> (stats) + score_kernel<D,true> (finish): one bkv_score call",
+    stats_kernel = ("qs_stats_kernel<D,BPW>" if w.group * w.window + w.nb_max <= 256 else "score_kernel<D,false>")
+    roof = {"kernel": {"score": f"{stats_kernel} (stats) + score_kernel<D,true> (finish): one bkv_score call",
                        "select": "select_topk_kernel (bkv_select_topk)",
                        "compact": "compact_kernel (bkv_compact)",
                        "update_beacons": "fps_kernel (bkv_update_beacons)"}[dom],
@@ -232,6 +263,11 @@ def main():
         "per_call_ms": {n: round(t, 4) for n, t in per.items()},
         "roofline": roof,
     }
+    # Same-run ceiling: a plain read+write device copy of 4 GiB moved.
+    ceil = copy_ceiling(dev)
+    out["copy_ceiling_gbs"] = round(ceil, 1)
+    out["hbm_alg_frac_of_copy_ceiling"] = round(total_bytes / (ms * 1e-3) / 1e9 / ceil, 4)
+    log(f"[bench] copy ceiling {ceil:.0f} GB/s")
     if args.copy_calibration:
         n = 1 << 28   # 1 GiB of float32
         src = torch.ones(n, device=dev)
