@@ -100,13 +100,11 @@ struct Smem {
   float* st_m;   // [kWaves][2][obs_pad] (stats pass): per wave and lane half
   float* st_z;   // [kWaves][2][obs_pad] (stats pass)
   float* nlse;   // [obs_pad]            (finish pass; aliases st_m): -lse2_i / c
-  float* lse_s;
   __device__ Smem(uint8_t* base, int obs_pad) {
     qs = base;
     st_m = reinterpret_cast<float*>(base + obs_pad * (D * 2));
     st_z = st_m + 2 * kWaves * obs_pad;
     nlse = st_m;
-    lse_s = st_m;
   }
 };
 
@@ -150,11 +148,9 @@ __device__ inline void load_qfrag(const uint8_t* qs, int qb, bf16x8 (&qf)[D / 16
 
 // ---- key fragments ----------------------------------------------------------------------
 //
-// A wave takes the 64 keys it owns in a tile as two 32-key fragments, one after the other.
-// Three fragment buffers rotate: while fragment j is multiplied against every row block,
-// the loads of fragments j+1 and j+2 are in flight, so keys are requested two whole
-// fragment passes before their use and the bursts of reads from every wave at once have
-// time to drain.
+// A wave takes the 64 keys it owns in a tile as two 32-key fragments, one after the other;
+// each fragment's registers are refilled with the next tile's fragment as soon as it has
+// been multiplied against every row block, a whole fragment pass before its use.
 
 // One 32-key fragment: lane l holds key (l & 31) and, for k-step s, dims 16*s + 8*(l >> 5)
 // .. +7 (the A layout of keys in the stats pass and the B layout in the finish pass are
@@ -173,31 +169,6 @@ __device__ inline void load_frag(const uint16_t* kp, int key0, int L, Frag<D>& f
   const uint16_t* src = kp + static_cast<size_t>(key) * D + (lane >> 5) * 8;
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) f.v[s] = *reinterpret_cast<const bf16x8*>(src + s * 16);
-}
-
-// First key of fragment j of a segment that starts at tile tile0 and has nfrag fragments;
-// indices past the end give the last fragment again, so the loads stay unconditional.
-__device__ inline int frag_key(int tile0, int nfrag, int j) {
-  j = j < nfrag ? j : nfrag - 1;
-  return (tile0 + (j >> 1)) * kScoreTile + (threadIdx.x >> 6) * 64 + (j & 1) * 32;
-}
-
-template <int D>
-__device__ inline void pipeline_start(const uint16_t* kp, int L, int tile0, int nfrag, Frag<D> (&f)[3]) {
-#pragma unroll
-  for (int i = 0; i < 3; ++i) load_frag<D>(kp, frag_key(tile0, nfrag, i), L, f[i]);
-}
-
-// pass(frag, key0) for every fragment of the segment, in order.
-template <int D, class Pass>
-__device__ inline void pipeline_run(const uint16_t* kp, int L, int tile0, int nfrag, Frag<D> (&f)[3], Pass&& pass) {
-  for (int j = 0; j < nfrag; j += 3) {
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      if (j + i < nfrag) pass(f[i], frag_key(tile0, nfrag, j + i));
-      load_frag<D>(kp, frag_key(tile0, nfrag, j + i + 3), L, f[i]);
-    }
-  }
 }
 
 // ---- stats pass -------------------------------------------------------------------------
@@ -378,34 +349,34 @@ __device__ void stats_segment(const ScoreArgs& a, const UnitInfo& ui, int tile0,
 
 // ---- finish pass ------------------------------------------------------------------------
 
-// Row log2-sum-exp2 for the rows a lane's accumulators hold in the finish layout: register
-// r = 4g + j of lane l is row 8g + 4(l >> 5) + j of the block.
-struct RowLse {
-  float4 g[4];
-};
-
-__device__ inline void load_lse(const float* lse_s, int qb, RowLse& out) {
+// The accumulators of a block start at -lse2_i / c instead of zero (c = log2(e) / sqrt(d)
+// > 0), so they end at x_ij - lse2_i / c and the vector work per logit is a running max;
+// score_j = exp2(c * max) once per key.  Register r = 4g + j of lane l is row
+// 8g + 4(l >> 5) + j of the block.
+__device__ inline f32x16 load_seed(const float* nlse, int qb) {
   const int lane = threadIdx.x & 63;
-  const float* p = lse_s + qb * 32 + 4 * (lane >> 5);
+  const float* p = nlse + qb * 32 + 4 * (lane >> 5);
+  f32x16 o;
 #pragma unroll
-  for (int g = 0; g < 4; ++g) out.g[g] = *reinterpret_cast<const float4*>(p + 8 * g);
+  for (int g = 0; g < 4; ++g) {
+    const float4 v = *reinterpret_cast<const float4*>(p + 8 * g);
+    o[4 * g] = v.x;
+    o[4 * g + 1] = v.y;
+    o[4 * g + 2] = v.z;
+    o[4 * g + 3] = v.w;
+  }
+  return o;
 }
 
-__device__ inline float lse_at(const RowLse& l, int r) {
-  const float4 v = l.g[r >> 2];
-  return (r & 3) == 0 ? v.x : (r & 3) == 1 ? v.y : (r & 3) == 2 ? v.z : v.w;
-}
-
-// Running max over rows of c * x - lse for the block in `cur` (fragment f in vm[f]) while
-// the products of the next block go into `nxt`; then rows nq*32.. are loaded into qf and
-// the next block's lse into lnext.
+// Running max over the rows of the block in `cur` (fragment f in vm[f]) while the
+// products of the next block (accumulators seeded with `seed`) go into `nxt`; then the
+// rows of block nq are loaded into qf and the seed of block nq into seed_next.
 template <int D>
 __device__ inline void finish_step(const KeyFrag<D>& kf, bf16x8 (&qf)[D / 16], const f32x16 (&cur)[2],
-                                   f32x16 (&nxt)[2], const RowLse& lcur, RowLse& lnext, const uint8_t* qs,
-                                   const float* lse_s, int qb_next, int nq, float c, float (&vm)[2]) {
-  f32x16 n0 = {}, n1 = {};
+                                   f32x16 (&nxt)[2], const f32x16& seed, f32x16& seed_next, const uint8_t* qs,
+                                   const float* nlse, int nq, float (&vm)[2]) {
+  f32x16 n0 = seed, n1 = seed;
   constexpr int kPer = 16 / (D / 16);   // (row, key) pairs of each fragment per MFMA step
-  load_lse(lse_s, qb_next, lnext);
 #pragma unroll
   for (int st = 0; st < D / 16; ++st) {
     n0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[st], kf.v[0][st], n0, 0, 0, 0);
@@ -413,47 +384,38 @@ __device__ inline void finish_step(const KeyFrag<D>& kf, bf16x8 (&qf)[D / 16], c
 #pragma unroll
     for (int f = 0; f < 2; ++f)
 #pragma unroll
-      for (int j = 0; j < kPer; j += 2) {
-        const int r = st * kPer + j;
-        const float t0 = fmaf(cur[f][r], c, -lse_at(lcur, r));
-        const float t1 = fmaf(cur[f][r + 1], c, -lse_at(lcur, r + 1));
-        vm[f] = fmaxf(vm[f], fmaxf(t0, t1));
-      }
+      for (int j = 0; j < kPer; j += 2) vm[f] = fmaxf(vm[f], fmaxf(cur[f][st * kPer + j], cur[f][st * kPer + j + 1]));
   }
 #pragma unroll
   for (int st = 0; st < D / 16; ++st) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);           // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x002, 3 * kPer, 0);    // VALU
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);       // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, kPer, 0);    // VALU
   }
+  seed_next = load_seed(nlse, nq);
   load_qfrag<D>(qs, nq, qf);
   nxt[0] = n0;
   nxt[1] = n1;
 }
 
-__device__ inline void finish_last(const f32x16 (&cur)[2], const RowLse& lcur, float c, float (&vm)[2]) {
+__device__ inline void finish_last(const f32x16 (&cur)[2], float (&vm)[2]) {
 #pragma unroll
   for (int f = 0; f < 2; ++f)
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const float t0 = fmaf(cur[f][r], c, -lse_at(lcur, r));
-      const float t1 = fmaf(cur[f][r + 1], c, -lse_at(lcur, r + 1));
-      vm[f] = fmaxf(vm[f], fmaxf(t0, t1));
-    }
+    for (int r = 0; r < 16; r += 2) vm[f] = fmaxf(vm[f], fmaxf(cur[f][r], cur[f][r + 1]));
 }
 
-// One wave's 64 keys: returns, in lane l, max over all rows of c * s - lse for key l of
+// One wave's 64 keys: returns, in lane l, max over all rows of x - lse2 / c for key l of
 // the wave (fragment l >> 5, key l & 31).
 template <int D>
-__device__ inline float finish_tile(const KeyFrag<D>& kf, const uint8_t* qs, const float* lse_s, int nqb, float c) {
+__device__ inline float finish_tile(const KeyFrag<D>& kf, const uint8_t* qs, const float* nlse, int nqb) {
   const int lane = threadIdx.x & 63;
   float vm[2] = {kNegInf, kNegInf};
   bf16x8 qf[D / 16];
   f32x16 A[2], B[2];
-  RowLse la, lb;
+  f32x16 sa = load_seed(nlse, 0);
   load_qfrag<D>(qs, 0, qf);
-  load_lse(lse_s, 0, la);
   {
-    f32x16 c0 = {}, c1 = {};
+    f32x16 c0 = sa, c1 = sa;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
       c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[s], kf.v[0][s], c0, 0, 0, 0);
@@ -462,17 +424,19 @@ __device__ inline float finish_tile(const KeyFrag<D>& kf, const uint8_t* qs, con
     A[0] = c0;
     A[1] = c1;
   }
-  load_qfrag<D>(qs, nqb > 1 ? 1 : 0, qf);
+  const int b1 = nqb > 1 ? 1 : 0;
+  f32x16 sb = load_seed(nlse, b1);
+  load_qfrag<D>(qs, b1, qf);
   int qb = 0;
   for (; qb + 2 < nqb; qb += 2) {
-    finish_step<D>(kf, qf, A, B, la, lb, qs, lse_s, qb + 1, qb + 2, c, vm);
-    finish_step<D>(kf, qf, B, A, lb, la, qs, lse_s, qb + 2, qb + 3 < nqb ? qb + 3 : nqb - 1, c, vm);
+    finish_step<D>(kf, qf, A, B, sb, sa, qs, nlse, qb + 2, vm);
+    finish_step<D>(kf, qf, B, A, sa, sb, qs, nlse, qb + 3 < nqb ? qb + 3 : nqb - 1, vm);
   }
   if (qb + 1 < nqb) {
-    finish_step<D>(kf, qf, A, B, la, lb, qs, lse_s, qb + 1, qb + 1, c, vm);
-    finish_last(B, lb, c, vm);
+    finish_step<D>(kf, qf, A, B, sb, sa, qs, nlse, qb + 1, vm);
+    finish_last(B, vm);
   } else {
-    finish_last(A, la, c, vm);
+    finish_last(A, vm);
   }
   // lanes l and l ^ 32 hold the two row halves of the same keys
   const bool lo = lane < 32;
@@ -510,8 +474,8 @@ __device__ void finish_segment(const ScoreArgs& a, const UnitInfo& ui, int tile0
 #pragma unroll
       for (int j = 0; j < 8; ++j) merge_stats(M, Z, pm[j], pz[j]);
     }
-    // Padding rows get +inf: they never win the max.
-    sm.lse_s[i] = (i < ui.n_obs && Z > 0.f) ? M + log2f(Z) : kPosInf;
+    // -lse2_i / c; padding rows -inf: they never win the max.
+    sm.nlse[i] = (i < ui.n_obs && Z > 0.f) ? -(M + log2f(Z)) / a.scale_log2 : kNegInf;
   }
   __syncthreads();
   const int t1 = tile0 + ntile;
@@ -520,9 +484,9 @@ __device__ void finish_segment(const ScoreArgs& a, const UnitInfo& ui, int tile0
     if (t > tile0) load_keys<D>(kp, kbase, ui.L, kf);
     if (kbase < ui.L) {
       float v = kNegInf;
-      if (ui.nqb > 0) v = finish_tile<D>(kf, sm.qs, sm.lse_s, ui.nqb, a.scale_log2);
+      if (ui.nqb > 0) v = finish_tile<D>(kf, sm.qs, sm.nlse, ui.nqb);
       const int key = kbase + lane;
-      if (key < ui.L) sp[key] = ui.n_obs > 0 ? exp2f(v) : 0.f;
+      if (key < ui.L) sp[key] = ui.n_obs > 0 ? exp2f(a.scale_log2 * v) : 0.f;
     }
   }
   __syncthreads();   // LDS is restaged by the next segment

@@ -18,7 +18,6 @@ constexpr int kThreads = kWaves * 64;
 static_assert(kScoreTile == kWaves * 64, "a tile is 64 keys per wave");
 
 constexpr float kNegInf = -__builtin_inff();
-constexpr float kPosInf = __builtin_inff();
 
 // ---- work split -----------------------------------------------------------------------
 
