@@ -28,10 +28,12 @@ LIB_PATH = os.path.join(_HERE, "libbkv.so")
 
 BKV_OK, BKV_EINVAL, BKV_EUNSUPPORTED, BKV_EALIAS, BKV_EWORKSPACE, BKV_EHIP = 0, -1, -2, -3, -4, -5
 MAX_OBS = 512
+AGG_MAX, AGG_MEAN = 0, 1
+AGGREGATIONS = {"max": AGG_MAX, "mean": AGG_MEAN}
 MAX_POOL = 768
 
 EXPORTS = ["bkv_status_string", "bkv_version", "bkv_last_error", "bkv_update_beacons", "bkv_score_workspace_bytes",
-           "bkv_score", "bkv_select_workspace_bytes", "bkv_select_topk", "bkv_compact",
+           "bkv_score", "bkv_score_agg", "bkv_select_workspace_bytes", "bkv_select_topk", "bkv_compact",
            "bkv_compress_workspace_bytes", "bkv_compress"]
 
 
@@ -76,6 +78,8 @@ def load() -> ctypes.CDLL:
     lib.bkv_score_workspace_bytes.argtypes = [P(_Shape), i32, i32]
     lib.bkv_score.restype = ctypes.c_int
     lib.bkv_score.argtypes = [P(_Shape), arr, arr, i32, i32, arr, arr, i32, arr, vp, sz, vp]
+    lib.bkv_score_agg.restype = ctypes.c_int
+    lib.bkv_score_agg.argtypes = [P(_Shape), arr, arr, i32, i32, arr, arr, i32, ctypes.c_int, arr, vp, sz, vp]
     lib.bkv_select_workspace_bytes.restype = sz
     lib.bkv_select_workspace_bytes.argtypes = [P(_Shape), i32]
     lib.bkv_select_topk.restype = ctypes.c_int
@@ -223,20 +227,27 @@ def _score_inputs(s: CacheShape, k, q, q_len, window, beacons, n_beacons, nb_max
 
 
 def prepare_score(s: CacheShape, k, q, q_len: int, window: int, beacons, n_beacons, nb_max: int, scores,
-                  workspace: Optional[torch.Tensor]) -> Call:
+                  workspace: Optional[torch.Tensor], aggregation: str = "max") -> Call:
+    """bkv_score for max aggregation, bkv_score_agg for any other."""
     lib = load()
+    if aggregation not in AGGREGATIONS:
+        raise ValueError(f"aggregation must be one of {sorted(AGGREGATIONS)}, got {aggregation!r}")
     shape = s.c()
     kp, qp, bp, nbp = _score_inputs(s, k, q, q_len, window, beacons, n_beacons, nb_max)
     sp = _layers(scores, s.n_layers, torch.float32, (s.batch, s.n_kv_heads, s.capacity), "scores")
     wp, wn = _workspace(workspace, int(lib.bkv_score_workspace_bytes(ctypes.byref(shape), window, nb_max)))
-    args = (ctypes.byref(shape), kp, qp, q_len, window, bp, nbp, nb_max, sp, wp, wn)
-    return Call(lib.bkv_score, args, "bkv_score", (shape, s.seq_len, k, q, beacons, n_beacons, scores, workspace))
+    keep = (shape, s.seq_len, k, q, beacons, n_beacons, scores, workspace)
+    if aggregation == "max":
+        args = (ctypes.byref(shape), kp, qp, q_len, window, bp, nbp, nb_max, sp, wp, wn)
+        return Call(lib.bkv_score, args, "bkv_score", keep)
+    args = (ctypes.byref(shape), kp, qp, q_len, window, bp, nbp, nb_max, AGGREGATIONS[aggregation], sp, wp, wn)
+    return Call(lib.bkv_score_agg, args, "bkv_score_agg", keep)
 
 
 def score(s: CacheShape, k, q, q_len: int, window: int, beacons, n_beacons, nb_max: int, scores,
-          workspace: Optional[torch.Tensor], stream=None) -> None:
-    """Max-aggregated attention scores of every cached key (bkv_score)."""
-    prepare_score(s, k, q, q_len, window, beacons, n_beacons, nb_max, scores, workspace)(stream)
+          workspace: Optional[torch.Tensor], stream=None, aggregation: str = "max") -> None:
+    """Attention scores of every cached key, max- (bkv_score) or mean-aggregated (bkv_score_agg)."""
+    prepare_score(s, k, q, q_len, window, beacons, n_beacons, nb_max, scores, workspace, aggregation)(stream)
 
 
 def prepare_select_topk(s: CacheShape, scores, budget: int, window: int, idx, n_kept) -> Call:

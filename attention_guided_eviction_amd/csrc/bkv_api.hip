@@ -184,6 +184,15 @@ size_t bkv_score_workspace_bytes(const bkv_shape* shape, int32_t window, int32_t
 bkv_status bkv_score(const bkv_shape* shape, const void* const* k, const void* const* q, int32_t q_len,
                      int32_t window, const void* const* beacons, const int32_t* const* n_beacons, int32_t nb_max,
                      float* const* scores, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return bkv_score_agg(shape, k, q, q_len, window, beacons, n_beacons, nb_max, BKV_AGG_MAX, scores, workspace,
+                       workspace_bytes, stream);
+}
+
+bkv_status bkv_score_agg(const bkv_shape* shape, const void* const* k, const void* const* q, int32_t q_len,
+                         int32_t window, const void* const* beacons, const int32_t* const* n_beacons, int32_t nb_max,
+                         bkv_aggregation aggregation, float* const* scores, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  if (aggregation != BKV_AGG_MAX && aggregation != BKV_AGG_MEAN) return BKV_EINVAL;
   bkv_status st = check_score_args(shape, k, q, q_len, window, beacons, n_beacons, nb_max, scores);
   if (st != BKV_OK) return st;
   const ScoreWs ws = score_ws(shape, window, nb_max);
@@ -206,6 +215,7 @@ bkv_status bkv_score(const bkv_shape* shape, const void* const* k, const void* c
   a.nb_max = nb_max;
   a.obs_pad = obs_pad_of(shape, window, nb_max);
   a.scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(shape->head_dim)));
+  a.mean = aggregation == BKV_AGG_MEAN ? 1 : 0;
   for (int l0 = 0; l0 < shape->n_layers; l0 += kMaxLayers) {
     const int nl = std::min(kMaxLayers, shape->n_layers - l0);
     for (int i = 0; i < nl; ++i) {

@@ -35,6 +35,7 @@ struct ScoreArgs {
   int obs_pad;          // observation rows per unit rounded up to 32 (launch-wide)
   int slots;            // statistics slots per unit (set by the launcher)
   int paired;           // two workgroups per CU, w and w + grid/2 (set by the launcher)
+  int mean;             // 1: mean of the observation rows' attention weights, 0: max
   float scale_log2;     // log2(e) / sqrt(head_dim)
 };
 

@@ -368,13 +368,22 @@ __device__ inline f32x16 load_seed(const float* nlse, int qb) {
   return o;
 }
 
-// Running max over the rows of the block in `cur` (fragment f in vm[f]) while the
-// products of the next block (accumulators seeded with `seed`) go into `nxt`; then the
-// rows of block nq are loaded into qf and the seed of block nq into seed_next.
-template <int D>
+// Folds the block in `cur` into vm[f] (fragment f) while the products of the next block
+// (accumulators seeded with `seed`) go into `nxt`; then the rows of block nq are loaded
+// into qf and the seed of block nq into seed_next.  MEAN: vm sums the attention weights
+// exp2(c * acc); otherwise vm is the running max of acc.
+template <bool MEAN>
+__device__ inline void fold2(float& vm, float x0, float x1, float c) {
+  if (MEAN)
+    vm += __builtin_amdgcn_exp2f(c * x0) + __builtin_amdgcn_exp2f(c * x1);
+  else
+    vm = fmaxf(vm, fmaxf(x0, x1));
+}
+
+template <int D, bool MEAN>
 __device__ inline void finish_step(const KeyFrag<D>& kf, bf16x8 (&qf)[D / 16], const f32x16 (&cur)[2],
                                    f32x16 (&nxt)[2], const f32x16& seed, f32x16& seed_next, const uint8_t* qs,
-                                   const float* nlse, int nq, float (&vm)[2]) {
+                                   const float* nlse, int nq, float c, float (&vm)[2]) {
   f32x16 n0 = seed, n1 = seed;
   constexpr int kPer = 16 / (D / 16);   // (row, key) pairs of each fragment per MFMA step
 #pragma unroll
@@ -384,12 +393,12 @@ __device__ inline void finish_step(const KeyFrag<D>& kf, bf16x8 (&qf)[D / 16], c
 #pragma unroll
     for (int f = 0; f < 2; ++f)
 #pragma unroll
-      for (int j = 0; j < kPer; j += 2) vm[f] = fmaxf(vm[f], fmaxf(cur[f][st * kPer + j], cur[f][st * kPer + j + 1]));
+      for (int j = 0; j < kPer; j += 2) fold2<MEAN>(vm[f], cur[f][st * kPer + j], cur[f][st * kPer + j + 1], c);
   }
 #pragma unroll
   for (int st = 0; st < D / 16; ++st) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);       // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x002, kPer, 0);    // VALU
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                          // MFMA
+    __builtin_amdgcn_sched_group_barrier(MEAN ? 0x402 : 0x002, MEAN ? 3 * kPer : kPer, 0);   // VALU
   }
   seed_next = load_seed(nlse, nq);
   load_qfrag<D>(qs, nq, qf);
@@ -397,19 +406,21 @@ __device__ inline void finish_step(const KeyFrag<D>& kf, bf16x8 (&qf)[D / 16], c
   nxt[1] = n1;
 }
 
-__device__ inline void finish_last(const f32x16 (&cur)[2], float (&vm)[2]) {
+template <bool MEAN>
+__device__ inline void finish_last(const f32x16 (&cur)[2], float c, float (&vm)[2]) {
 #pragma unroll
   for (int f = 0; f < 2; ++f)
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) vm[f] = fmaxf(vm[f], fmaxf(cur[f][r], cur[f][r + 1]));
+    for (int r = 0; r < 16; r += 2) fold2<MEAN>(vm[f], cur[f][r], cur[f][r + 1], c);
 }
 
-// One wave's 64 keys: returns, in lane l, max over all rows of x - lse2 / c for key l of
-// the wave (fragment l >> 5, key l & 31).
-template <int D>
-__device__ inline float finish_tile(const KeyFrag<D>& kf, const uint8_t* qs, const float* nlse, int nqb) {
+// One wave's 64 keys: returns, in lane l, for key l of the wave (fragment l >> 5, key
+// l & 31) the max over all rows of x - lse2 / c, or with MEAN the sum over all rows of the
+// attention weights.
+template <int D, bool MEAN>
+__device__ inline float finish_tile(const KeyFrag<D>& kf, const uint8_t* qs, const float* nlse, int nqb, float c) {
   const int lane = threadIdx.x & 63;
-  float vm[2] = {kNegInf, kNegInf};
+  float vm[2] = {MEAN ? 0.f : kNegInf, MEAN ? 0.f : kNegInf};
   bf16x8 qf[D / 16];
   f32x16 A[2], B[2];
   f32x16 sa = load_seed(nlse, 0);
@@ -429,25 +440,25 @@ __device__ inline float finish_tile(const KeyFrag<D>& kf, const uint8_t* qs, con
   load_qfrag<D>(qs, b1, qf);
   int qb = 0;
   for (; qb + 2 < nqb; qb += 2) {
-    finish_step<D>(kf, qf, A, B, sb, sa, qs, nlse, qb + 2, vm);
-    finish_step<D>(kf, qf, B, A, sa, sb, qs, nlse, qb + 3 < nqb ? qb + 3 : nqb - 1, vm);
+    finish_step<D, MEAN>(kf, qf, A, B, sb, sa, qs, nlse, qb + 2, c, vm);
+    finish_step<D, MEAN>(kf, qf, B, A, sa, sb, qs, nlse, qb + 3 < nqb ? qb + 3 : nqb - 1, c, vm);
   }
   if (qb + 1 < nqb) {
-    finish_step<D>(kf, qf, A, B, sb, sa, qs, nlse, qb + 1, vm);
-    finish_last(B, vm);
+    finish_step<D, MEAN>(kf, qf, A, B, sb, sa, qs, nlse, qb + 1, c, vm);
+    finish_last<MEAN>(B, c, vm);
   } else {
-    finish_last(A, vm);
+    finish_last<MEAN>(A, c, vm);
   }
   // lanes l and l ^ 32 hold the two row halves of the same keys
   const bool lo = lane < 32;
   const float keep = lo ? vm[0] : vm[1];
-  const float send = lo ? vm[1] : vm[0];
-  return fmaxf(keep, __shfl_xor(send, 32));
+  const float other = __shfl_xor(lo ? vm[1] : vm[0], 32);
+  return MEAN ? keep + other : fmaxf(keep, other);
 }
 
 // Scores of tiles tile0 .. tile0+ntile-1 of one unit.  Its statistics partials are the
 // n_part slots at pm0/pz0 (stride obs_pad), slot s written by workgroup w0 + s.
-template <int D>
+template <int D, bool MEAN>
 __device__ void finish_segment(const ScoreArgs& a, const UnitInfo& ui, int tile0, int ntile, const float* pm0,
                                const float* pz0, int n_part, uint8_t* smem) {
   Smem<D> sm(smem, a.obs_pad);
@@ -484,9 +495,9 @@ __device__ void finish_segment(const ScoreArgs& a, const UnitInfo& ui, int tile0
     if (t > tile0) load_keys<D>(kp, kbase, ui.L, kf);
     if (kbase < ui.L) {
       float v = kNegInf;
-      if (ui.nqb > 0) v = finish_tile<D>(kf, sm.qs, sm.nlse, ui.nqb);
+      if (ui.nqb > 0) v = finish_tile<D, MEAN>(kf, sm.qs, sm.nlse, ui.nqb, a.scale_log2);
       const int key = kbase + lane;
-      if (key < ui.L) sp[key] = ui.n_obs > 0 ? exp2f(a.scale_log2 * v) : 0.f;
+      if (key < ui.L) sp[key] = ui.n_obs > 0 ? (MEAN ? v / static_cast<float>(ui.n_obs) : exp2f(a.scale_log2 * v)) : 0.f;
     }
   }
   __syncthreads();   // LDS is restaged by the next segment
@@ -495,7 +506,7 @@ __device__ void finish_segment(const ScoreArgs& a, const UnitInfo& ui, int tile0
 // ---- kernels ----------------------------------------------------------------------------
 
 
-template <int D, bool FINISH>
+template <int D, bool FINISH, bool MEAN = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void score_kernel(const ScoreArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int w = static_cast<int>(blockIdx.x);
@@ -529,7 +540,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
     if (FINISH) {
       int n_part = ss.owner(first + cur.nt - 1) - w0 + 1;
       n_part = n_part < a.slots ? n_part : a.slots;
-      finish_segment<D>(a, ui, cur.tile, n, a.part_m + unit_part, a.part_z + unit_part, n_part, smem);
+      finish_segment<D, MEAN>(a, ui, cur.tile, n, a.part_m + unit_part, a.part_z + unit_part, n_part, smem);
     } else if (w - w0 < a.slots) {
       const size_t o = unit_part + static_cast<size_t>(w - w0) * a.obs_pad;
       stats_segment<D>(a, ui, cur.tile, n, a.part_m + o, a.part_z + o, smem);
@@ -552,6 +563,9 @@ hipError_t launch_d(ScoreArgs a, int n_layers, hipStream_t s) {
                                    hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (attr_err == hipSuccess)
       attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&score_kernel<D, true>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (attr_err == hipSuccess)
+      attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&score_kernel<D, true, true>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   });
   if (attr_err != hipSuccess) return note_hip_error(attr_err, "score: hipFuncSetAttribute");
@@ -585,7 +599,10 @@ hipError_t launch_d(ScoreArgs a, int n_layers, hipStream_t s) {
     e = hipGetLastError();
     if (e != hipSuccess) return note_hip_error(e, "score: launch score_stats");
   }
-  hipLaunchKernelGGL((score_kernel<D, true>), dim3(grid), dim3(kThreads), lds, s, a);
+  if (a.mean)
+    hipLaunchKernelGGL((score_kernel<D, true, true>), dim3(grid), dim3(kThreads), lds, s, a);
+  else
+    hipLaunchKernelGGL((score_kernel<D, true>), dim3(grid), dim3(kThreads), lds, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return note_hip_error(e, "score: launch score_finish");
   return hipSuccess;

@@ -28,6 +28,7 @@ class EventConfig:
     nb_max: int         # beacon slots per KV head
     budget: int         # kept keys per KV head (window included)
     t_new: int = 0      # new queries per head fed to the beacon update (0: no update)
+    aggregation: str = "max"   # "max" (the method) or "mean" (Table 2's alternative)
 
 
 class CompressionEvent:
@@ -69,17 +70,22 @@ class CompressionEvent:
                                                       self.v_out, self.workspace)
         # the three stages of compress, separately (for per-stage timing)
         self.calls["score"] = bkv.prepare_score(sh, k, q, c.q_len, c.window, beacons, n_beacons, c.nb_max,
-                                                self.scores, self.workspace)
+                                                self.scores, self.workspace, c.aggregation)
         self.calls["select"] = bkv.prepare_select_topk(sh, self.scores, c.budget, c.window, self.idx, self.n_kept)
         self.calls["compact"] = bkv.prepare_compact(sh, k, v, self.idx, self.n_kept, c.budget, self.k_out,
                                                     self.v_out)
         return self
 
     def step(self, stream=None) -> None:
-        """One event over the bound inputs: beacon update (if configured), then compress."""
+        """One event over the bound inputs: beacon update (if configured), then compress
+        (max aggregation) or score, select and compact (any other aggregation)."""
         if "update_beacons" in self.calls:
             self.calls["update_beacons"](stream)
-        self.calls["compress"](stream)
+        if self.cfg.aggregation == "max":
+            self.calls["compress"](stream)
+        else:
+            for name in ("score", "select", "compact"):
+                self.calls[name](stream)
 
     def run(self, k, v, q, beacons, n_beacons, stream=None) -> None:
         """Bind the inputs and run one event."""

@@ -41,6 +41,8 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device copy five times (a known-size reference for the "
                             "FETCH_SIZE / WRITE_SIZE counters)")
+    p.add_argument("--aggregation", default="max", choices=["max", "mean"],
+                   help="score aggregation over the observation rows (the method: max; Table 2: mean)")
     p.add_argument("--quiet", action="store_true")
     return p.parse_args()
 
@@ -191,7 +193,7 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] inputs for {w.name} built in {time.time() - t0:.1f}s")
     cfg = EventConfig(w.n_layers, w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.capacity, w.q_len, w.window,
-                      w.nb_max, w.budget, w.t_new)
+                      w.nb_max, w.budget, w.t_new, args.aggregation)
     ev = CompressionEvent(cfg, seq_len, dev)
     stream = torch.cuda.current_stream()
     k, v, q, bc, nb = inp["k"], inp["v"], inp["q"], inp["beacons"], inp["n_beacons"]
@@ -257,7 +259,8 @@ def main():
         "config": {"workload": w.name, "layers": w.n_layers, "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads,
                    "head_dim": w.head_dim, "batch": w.batch, "seq_len": int(lens.max()) if w.ragged is None
                    else f"ragged {w.ragged[0]}-{w.ragged[1]} (sum {int(lens.sum())})",
-                   "window": w.window, "beacons": w.nb_max, "budget": w.budget, "beacon_update_queries": w.t_new},
+                   "window": w.window, "beacons": w.nb_max, "budget": w.budget, "beacon_update_queries": w.t_new,
+                   "aggregation": args.aggregation},
         "hbm_alg_gbs": round(total_bytes / (ms * 1e-3) / 1e9, 1),
         "hbm_alg_frac_of_peak": round(total_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "per_call_ms": {n: round(t, 4) for n, t in per.items()},

@@ -11,6 +11,7 @@
  *   bkv_score           attention-based score of every cached key from the recent queries
  *                       and the beacon queries (Figure 5 (b)), max-aggregated over queries
  *                       and heads (Figure 5 (c); Table 2 caption);
+ *   bkv_score_agg       the same scores with max or mean aggregation (Table 2);
  *   bkv_select_topk     top-K under the cache budget (Figure 5 (c)), the recent window
  *                       always kept;
  *   bkv_compact         eviction: the kept K/V rows gathered into a compacted cache
@@ -151,6 +152,12 @@ bkv_status bkv_update_beacons(const bkv_shape* shape,
  * ---------------------------------------------------------------------------------- */
 size_t bkv_score_workspace_bytes(const bkv_shape* shape, int32_t window, int32_t nb_max);
 
+/* How the observation rows' attention weights of a key combine into its score. */
+typedef enum {
+  BKV_AGG_MAX = 0,  /* largest weight (the method's choice; Figure 5 (c)) */
+  BKV_AGG_MEAN = 1  /* mean weight over the observation rows (Table 2's alternative) */
+} bkv_aggregation;
+
 bkv_status bkv_score(const bkv_shape* shape,
                      const void* const* k,
                      const void* const* q, int32_t q_len, int32_t window,
@@ -158,6 +165,28 @@ bkv_status bkv_score(const bkv_shape* shape,
                      float* const* scores,
                      void* workspace, size_t workspace_bytes,
                      hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * Attention-based key scores with a chosen aggregation.
+ * BeaconKV page, Table 2 (max vs. mean aggregation, applied alike across heads and
+ * queries).
+ *
+ * As bkv_score, with the score of key j
+ *     BKV_AGG_MAX:  max_i w_ij                      (identical to bkv_score)
+ *     BKV_AGG_MEAN: (1 / n_obs) * sum_i w_ij
+ * where w_ij = exp(s_ij - logsumexp_j' s_ij') over the unit's n_obs observation rows
+ * (G * window recent queries and the live beacons); with n_obs = 0 every valid score is
+ * 0.  Under BKV_AGG_MEAN a unit's scores sum to 1 over its valid keys.  Same arguments,
+ * workspace and errors as bkv_score, plus BKV_EINVAL for an unknown aggregation.
+ * ---------------------------------------------------------------------------------- */
+bkv_status bkv_score_agg(const bkv_shape* shape,
+                         const void* const* k,
+                         const void* const* q, int32_t q_len, int32_t window,
+                         const void* const* beacons, const int32_t* const* n_beacons, int32_t nb_max,
+                         bkv_aggregation aggregation,
+                         float* const* scores,
+                         void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
  * Top-K selection under the budget with the recent window always kept.

@@ -109,6 +109,28 @@ def max_aggregated_scores(obs: np.ndarray, keys: np.ndarray) -> np.ndarray:
     return attention_probabilities(obs, keys).max(axis=0)
 
 
+def mean_aggregated_scores(obs: np.ndarray, keys: np.ndarray) -> np.ndarray:
+    """Per-key score [L]: the mean attention weight over the observation queries.
+
+    Table 2 compares max aggregation with mean aggregation, each applied the same way
+    across heads and queries; the mean therefore runs over the same rows as the max
+    (every query of the GQA group and every beacon of the KV head).  An empty
+    observation set gives every key 0, as for the max.
+    """
+    if keys.shape[0] == 0 or obs.shape[0] == 0:
+        return np.zeros(keys.shape[0])
+    return attention_probabilities(obs, keys).mean(axis=0)
+
+
+def aggregated_scores(obs: np.ndarray, keys: np.ndarray, aggregation: str = "max") -> np.ndarray:
+    """Max (Figure 5 (c)) or mean (Table 2) aggregated scores."""
+    if aggregation == "max":
+        return max_aggregated_scores(obs, keys)
+    if aggregation == "mean":
+        return mean_aggregated_scores(obs, keys)
+    raise ValueError(f"unknown aggregation {aggregation!r}")
+
+
 # ---------------------------------------------------------------------------------------------
 # Selection (Figure 5 (c)) and eviction (Abstract)
 # ---------------------------------------------------------------------------------------------

@@ -38,9 +38,9 @@ def log(*a):
     sys.stdout.flush()
 
 
-def event_config(w: Workload) -> EventConfig:
+def event_config(w: Workload, aggregation: str = "max") -> EventConfig:
     return EventConfig(w.n_layers, w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.capacity, w.q_len, w.window,
-                       w.nb_max, w.budget, w.t_new)
+                       w.nb_max, w.budget, w.t_new, aggregation)
 
 
 def build_inputs(w: Workload, device="cuda") -> Dict[str, List[torch.Tensor]]:
@@ -50,10 +50,10 @@ def build_inputs(w: Workload, device="cuda") -> Dict[str, List[torch.Tensor]]:
     return out
 
 
-def run_gpu(w: Workload, inputs=None, device="cuda") -> Tuple[CompressionEvent, Dict]:
+def run_gpu(w: Workload, inputs=None, device="cuda", aggregation: str = "max") -> Tuple[CompressionEvent, Dict]:
     if inputs is None:
         inputs = build_inputs(w, device)
-    ev = CompressionEvent(event_config(w), inputs["seq_len"], device)
+    ev = CompressionEvent(event_config(w, aggregation), inputs["seq_len"], device)
     ev.run(inputs["k"], inputs["v"], inputs["q"], inputs["beacons"], inputs["n_beacons"])
     torch.cuda.synchronize()
     return ev, inputs
@@ -131,6 +131,7 @@ def check_selection(keep_gpu: np.ndarray, s_gpu: np.ndarray, s_or: np.ndarray, L
 
 
 def check_unit(w: Workload, ev: CompressionEvent, layer: int, b: int, h: int) -> Dict[str, float]:
+    """One unit's beacons, scores (under the event's aggregation), selection and compaction."""
     u = unit_inputs(w, layer, b, h, "cpu")
     L = u["L"]
     kb, vb, qb, bcb = bf16_bits(u["k"]), bf16_bits(u["v"]), bf16_bits(u["q"]), bf16_bits(u["beacons"])
@@ -148,7 +149,7 @@ def check_unit(w: Workload, ev: CompressionEvent, layer: int, b: int, h: int) ->
         beacons_used, nb_used = bcb, u["nb"]
     # scores
     obs = O.observation_queries(O.bf16_to_f64(qb), w.window, O.bf16_to_f64(beacons_used), nb_used)
-    s_or = O.max_aggregated_scores(obs, O.bf16_to_f64(kb))
+    s_or = O.aggregated_scores(obs, O.bf16_to_f64(kb), ev.cfg.aggregation)
     s_gpu = ev.scores[layer][b, h, :L].cpu().numpy()
     if L:
         zero = s_or == 0.0

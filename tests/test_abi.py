@@ -149,3 +149,26 @@ def test_update_beacons_rejects():
     assert f(ctypes.byref(s), bi, ni, 16, qn, 128, 128, qn, no, None) == bkv.BKV_EALIAS
     assert f(ctypes.byref(s), bi, ni, 16, nulls(), 128, 128, bo, no, None) == bkv.BKV_EINVAL
     assert f(ctypes.byref(shape(head_dim=32)), bi, ni, 16, qn, 128, 128, bo, no, None) == bkv.BKV_EUNSUPPORTED
+
+
+def test_score_agg_rejects_unknown_aggregation_and_validates_like_score():
+    lib = bkv.load()
+    s = shape()
+
+    def call(agg, **kw):
+        a = dict(k=arr(FAKE + (1 << 36)), q=arr(FAKE + (2 << 36)), bc=arr(FAKE + (3 << 36)),
+                 nb=arr(FAKE + (4 << 36)), sc=arr(FAKE + (5 << 36)), window=32)
+        a.update(kw)
+        return lib.bkv_score_agg(ctypes.byref(s), a["k"], a["q"], 32, a["window"], a["bc"], a["nb"], 16, agg,
+                                 a["sc"], FAKE + (1 << 40), 1 << 40, None)
+
+    assert call(2) == bkv.BKV_EINVAL
+    assert call(-1) == bkv.BKV_EINVAL
+    assert call(bkv.AGG_MEAN, window=33) == bkv.BKV_EINVAL
+    assert call(bkv.AGG_MEAN, sc=arr(FAKE + (1 << 36) + 4096)) == bkv.BKV_EALIAS
+
+
+def test_header_aggregation_values_match_binding():
+    text = open(HEADER).read()
+    assert int(re.search(r"BKV_AGG_MAX = (\d+)", text).group(1)) == bkv.AGG_MAX
+    assert int(re.search(r"BKV_AGG_MEAN = (\d+)", text).group(1)) == bkv.AGG_MEAN

@@ -369,3 +369,60 @@ def test_compress_unit_window_and_count():
     assert r["keep"].size == 64 and set(range(296, 300)) <= set(r["keep"].tolist())
     np.testing.assert_array_equal(r["k_out"], k[r["keep"]])
     np.testing.assert_array_equal(r["v_out"], v[r["keep"]])
+
+
+# ------------------------------------------------------------------------------------------------
+# mean aggregation (Table 2)
+# ------------------------------------------------------------------------------------------------
+
+def test_mean_scores_closed_form_fixture():
+    g = _golden("scores_orthogonal_mean.json")
+    s = O.mean_aggregated_scores(np.array(g["queries"], float), np.array(g["keys"], float))
+    np.testing.assert_allclose(s, g["scores"], rtol=1e-14)
+
+
+@pytest.mark.parametrize("n_obs,L,d", [(1, 7, 8), (5, 64, 32), (13, 200, 128)])
+def test_mean_scores_equal_torch_sdpa_column_mean(n_obs, L, d):
+    rng = np.random.default_rng(n_obs * 7 + L)
+    q = rng.standard_normal((n_obs, d)) * 2.0
+    k = rng.standard_normal((L, d)) * 2.0
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(k)[None], torch.eye(L, dtype=torch.float64)[None])[0]
+    np.testing.assert_allclose(O.mean_aggregated_scores(q, k), ref.numpy().mean(axis=0), rtol=1e-12, atol=1e-15)
+
+
+def test_mean_scores_sum_to_one_and_sit_between_max_over_n_and_max():
+    rng = np.random.default_rng(31)
+    for _ in range(20):
+        n, L, d = rng.integers(1, 30), rng.integers(1, 300), rng.choice([8, 64, 128])
+        q = rng.standard_normal((n, d)) * rng.uniform(0.1, 4)
+        k = rng.standard_normal((L, d)) * rng.uniform(0.1, 4)
+        m = O.mean_aggregated_scores(q, k)
+        x = O.max_aggregated_scores(q, k)
+        np.testing.assert_allclose(m.sum(), 1.0, atol=1e-12)
+        assert np.all(m <= x * (1 + 1e-12)) and np.all(m >= x / n * (1 - 1e-12))
+
+
+def test_mean_equals_max_for_one_observer_and_zero_for_none():
+    rng = np.random.default_rng(32)
+    q = rng.standard_normal((1, 16))
+    k = rng.standard_normal((40, 16))
+    np.testing.assert_allclose(O.mean_aggregated_scores(q, k), O.max_aggregated_scores(q, k), rtol=1e-14)
+    np.testing.assert_array_equal(O.mean_aggregated_scores(q[:0], k), np.zeros(40))
+
+
+def test_mean_brute_force_pure_python():
+    rng = np.random.default_rng(33)
+    q = rng.standard_normal((4, 6))
+    k = rng.standard_normal((9, 6)) * 1.5
+    want = []
+    for j in range(9):
+        tot = 0.0
+        for i in range(4):
+            lg = [sum(q[i, t] * k[jj, t] for t in range(6)) / math.sqrt(6) for jj in range(9)]
+            tot += math.exp(lg[j]) / math.fsum(math.exp(x) for x in lg)
+        want.append(tot / 4)
+    np.testing.assert_allclose(O.mean_aggregated_scores(q, k), want, rtol=1e-13)
+    np.testing.assert_allclose(O.aggregated_scores(q, k, "mean"), want, rtol=1e-13)
+    with pytest.raises(ValueError):
+        O.aggregated_scores(q, k, "median")

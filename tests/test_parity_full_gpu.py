@@ -28,6 +28,17 @@ def test_full_size(name):
     torch.cuda.empty_cache()
 
 
+def test_full_size_mean_aggregation():
+    """Table 2's mean aggregation at the 7B shape's full size (sampled units)."""
+    w = WORKLOADS["qwen7b_16k"]
+    ev, inputs = run_gpu(w, aggregation="mean")
+    worst = check_units(w, ev, sample_units(w, 4, seed=99))
+    log(f"[full] qwen7b_16k mean: worst {worst}")
+    del ev, inputs
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
 def test_device_generation_matches_host():
     w = WORKLOADS["qwen4b_serving"].replace(n_layers=1, batch=3)
     from synth import layer_tensors

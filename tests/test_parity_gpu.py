@@ -10,10 +10,10 @@ from parity import all_units, check_units, log, run_gpu
 pytestmark = pytest.mark.gpu
 
 
-def _run_all(w):
+def _run_all(w, aggregation="max"):
     log(f"[parity] {w.name}: layers {w.n_layers} batch {w.batch} cap {w.capacity} window {w.window} "
-        f"nb {w.nb_init}/{w.nb_max} budget {w.budget} t_new {w.t_new}")
-    ev, _ = run_gpu(w)
+        f"nb {w.nb_init}/{w.nb_max} budget {w.budget} t_new {w.t_new} aggregation {aggregation}")
+    ev, _ = run_gpu(w, aggregation=aggregation)
     worst = check_units(w, ev, all_units(w))
     log(f"[parity] {w.name}: worst {worst}")
     return worst
@@ -83,3 +83,20 @@ def test_identical_keys_tie_to_lowest_positions():
     assert idx == list(range(w.budget - w.window)) + list(range(512 - w.window, 512))
     s = ev.scores[0][0, 0].cpu()
     assert torch.allclose(s, torch.full_like(s, 1 / 512), rtol=1e-5)
+
+
+# Mean aggregation (Table 2's alternative to the max): same kernels up to the finish pass.
+MEAN_CASES = {
+    "tiny": WORKLOADS["tiny"],
+    "qwen7b_reduced": WORKLOADS["qwen7b_16k"].replace(n_layers=2, capacity=3000, seq_len=2989, budget=700),
+    "qwen4b_ragged_fps": WORKLOADS["qwen4b_serving"].replace(n_layers=1, batch=3, capacity=2048, ragged=(700, 2048),
+                                                             budget=400),
+    "qwen14b_352_rows": WORKLOADS["qwen14b_64k"].replace(n_layers=1, capacity=2048, seq_len=2001, budget=512),
+    "lengths": EDGE["lengths"],
+    "no_observers": EDGE["no_observers"],
+}
+
+
+@pytest.mark.parametrize("case", sorted(MEAN_CASES))
+def test_mean_aggregation(case):
+    _run_all(MEAN_CASES[case].replace(name="mean_" + case), aggregation="mean")
