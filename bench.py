@@ -41,6 +41,10 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device copy five times (a known-size reference for the "
                             "FETCH_SIZE / WRITE_SIZE counters)")
+    p.add_argument("--window", type=int, default=None,
+                   help="override the workload's recent window W (queries per head, always-kept keys)")
+    p.add_argument("--beacons", type=int, default=None, help="override the beacons per KV head (live and slots)")
+    p.add_argument("--budget", type=int, default=None, help="override the kept keys per KV head")
     p.add_argument("--aggregation", default="max", choices=["max", "mean"],
                    help="score aggregation over the observation rows (the method: max; Table 2: mean)")
     p.add_argument("--quiet", action="store_true")
@@ -181,6 +185,12 @@ def main():
             print(*a, file=sys.stderr, flush=True)
 
     w = WORKLOADS[args.workload]
+    if args.window is not None:
+        w = w.replace(window=args.window)
+    if args.beacons is not None:
+        w = w.replace(nb_init=args.beacons, nb_max=args.beacons)
+    if args.budget is not None:
+        w = w.replace(budget=args.budget)
     bkv.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -235,7 +245,9 @@ def main():
     total_bytes = sum(ab.values())
     dom = max(per, key=per.get)
     achieved = ab[dom] / (per[dom] * 1e-3) / 1e9
-    traffic = score_traffic(w.name) if dom == "score" else None
+    # The committed counter summary holds for the workload as named, max aggregation.
+    as_named = args.window is None and args.beacons is None and args.budget is None and args.aggregation == "max"
+    traffic = score_traffic(w.name) if dom == "score" and as_named else None
     stats_kernel = ("qs_stats_kernel<D,BPW>" if w.group * w.window + w.nb_max <= 256 else "score_kernel<D,false>")
     roof = {"kernel": {"score": f"{stats_kernel} (stats) + score_kernel<D,true> (finish): one bkv_score call",
                        "select": "select_topk_kernel (bkv_select_topk)",

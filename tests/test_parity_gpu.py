@@ -100,3 +100,16 @@ MEAN_CASES = {
 @pytest.mark.parametrize("case", sorted(MEAN_CASES))
 def test_mean_aggregation(case):
     _run_all(MEAN_CASES[case].replace(name="mean_" + case), aggregation="mean")
+
+
+# Table 1's splits of the 32 observation slots per query step between recent queries and
+# beacons (n_recent, n_beacon), on the serving shape with the continual-FPS update.
+SPLITS = [(1, 31), (8, 24), (28, 4)]
+
+
+@pytest.mark.parametrize("n_recent,n_beacon", SPLITS)
+def test_recent_beacon_splits(n_recent, n_beacon):
+    w = WORKLOADS["qwen4b_serving"].replace(name=f"split_{n_recent}_{n_beacon}", n_layers=1, batch=3, capacity=2048,
+                                            ragged=(700, 2048), budget=512, window=n_recent, nb_init=n_beacon,
+                                            nb_max=n_beacon)
+    _run_all(w)
