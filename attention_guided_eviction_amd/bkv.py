@@ -30,9 +30,12 @@ BKV_OK, BKV_EINVAL, BKV_EUNSUPPORTED, BKV_EALIAS, BKV_EWORKSPACE, BKV_EHIP = 0, 
 MAX_OBS = 512
 AGG_MAX, AGG_MEAN = 0, 1
 AGGREGATIONS = {"max": AGG_MAX, "mean": AGG_MEAN}
+BEACON_FPS, BEACON_INITIAL = 0, 1
+BEACON_POLICIES = {"fps": BEACON_FPS, "initial": BEACON_INITIAL}
 MAX_POOL = 768
 
-EXPORTS = ["bkv_status_string", "bkv_version", "bkv_last_error", "bkv_update_beacons", "bkv_score_workspace_bytes",
+EXPORTS = ["bkv_status_string", "bkv_version", "bkv_last_error", "bkv_update_beacons", "bkv_update_beacons_policy",
+           "bkv_score_workspace_bytes",
            "bkv_score", "bkv_score_agg", "bkv_select_workspace_bytes", "bkv_select_topk", "bkv_compact",
            "bkv_compress_workspace_bytes", "bkv_compress"]
 
@@ -74,6 +77,8 @@ def load() -> ctypes.CDLL:
     lib.bkv_last_error.argtypes = []
     lib.bkv_update_beacons.restype = ctypes.c_int
     lib.bkv_update_beacons.argtypes = [P(_Shape), arr, arr, i32, arr, i32, i32, arr, arr, vp]
+    lib.bkv_update_beacons_policy.restype = ctypes.c_int
+    lib.bkv_update_beacons_policy.argtypes = [P(_Shape), arr, arr, i32, arr, i32, i32, ctypes.c_int, arr, arr, vp]
     lib.bkv_score_workspace_bytes.restype = sz
     lib.bkv_score_workspace_bytes.argtypes = [P(_Shape), i32, i32]
     lib.bkv_score.restype = ctypes.c_int
@@ -185,8 +190,11 @@ class Call:
 
 
 def prepare_update_beacons(s: CacheShape, beacons_in, n_in, nb_max: int, q_new, q_len: int, t_new: int,
-                           beacons_out, n_out) -> Call:
+                           beacons_out, n_out, policy: str = "fps") -> Call:
+    """bkv_update_beacons for continual FPS, bkv_update_beacons_policy for any other policy."""
     lib = load()
+    if policy not in BEACON_POLICIES:
+        raise ValueError(f"policy must be one of {sorted(BEACON_POLICIES)}, got {policy!r}")
     B, Hq, Hkv, D, n = s.batch, s.n_q_heads, s.n_kv_heads, s.head_dim, s.n_layers
     shape = s.c()
     bi = _layers(beacons_in, n, torch.bfloat16, (B, Hkv, nb_max, D), "beacons_in")
@@ -194,15 +202,19 @@ def prepare_update_beacons(s: CacheShape, beacons_in, n_in, nb_max: int, q_new, 
     qn = _layers(q_new, n, torch.bfloat16, (B, Hq, q_len, D), "q_new") if t_new > 0 else _null_layers(n)
     bo = _layers(beacons_out, n, torch.bfloat16, (B, Hkv, nb_max, D), "beacons_out")
     no = _layers(n_out, n, torch.int32, (B, Hkv), "n_out")
-    args = (ctypes.byref(shape), bi, ni, nb_max, qn, q_len, t_new, bo, no)
-    return Call(lib.bkv_update_beacons, args, "bkv_update_beacons",
-                (shape, s.seq_len, beacons_in, n_in, q_new, beacons_out, n_out))
+    keep = (shape, s.seq_len, beacons_in, n_in, q_new, beacons_out, n_out)
+    if policy == "fps":
+        args = (ctypes.byref(shape), bi, ni, nb_max, qn, q_len, t_new, bo, no)
+        return Call(lib.bkv_update_beacons, args, "bkv_update_beacons", keep)
+    args = (ctypes.byref(shape), bi, ni, nb_max, qn, q_len, t_new, BEACON_POLICIES[policy], bo, no)
+    return Call(lib.bkv_update_beacons_policy, args, "bkv_update_beacons_policy", keep)
 
 
 def update_beacons(s: CacheShape, beacons_in, n_in, nb_max: int, q_new, q_len: int, t_new: int,
-                   beacons_out, n_out, stream=None) -> None:
-    """Continual FPS update of the beacon sets of every layer (bkv_update_beacons)."""
-    prepare_update_beacons(s, beacons_in, n_in, nb_max, q_new, q_len, t_new, beacons_out, n_out)(stream)
+                   beacons_out, n_out, stream=None, policy: str = "fps") -> None:
+    """Beacon update of every layer: continual FPS (bkv_update_beacons) or the first
+    queries kept (bkv_update_beacons_policy, policy "initial")."""
+    prepare_update_beacons(s, beacons_in, n_in, nb_max, q_new, q_len, t_new, beacons_out, n_out, policy)(stream)
 
 
 def score_workspace_bytes(s: CacheShape, window: int, nb_max: int) -> int:

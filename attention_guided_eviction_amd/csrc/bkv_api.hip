@@ -295,6 +295,15 @@ bkv_status bkv_compact(const bkv_shape* shape, const void* const* k, const void*
 bkv_status bkv_update_beacons(const bkv_shape* shape, const void* const* beacons_in, const int32_t* const* n_in,
                               int32_t nb_max, const void* const* q_new, int32_t q_len, int32_t t_new,
                               void* const* beacons_out, int32_t* const* n_out, hipStream_t stream) {
+  return bkv_update_beacons_policy(shape, beacons_in, n_in, nb_max, q_new, q_len, t_new, BKV_BEACON_FPS, beacons_out,
+                                   n_out, stream);
+}
+
+bkv_status bkv_update_beacons_policy(const bkv_shape* shape, const void* const* beacons_in,
+                                     const int32_t* const* n_in, int32_t nb_max, const void* const* q_new,
+                                     int32_t q_len, int32_t t_new, bkv_beacon_policy policy,
+                                     void* const* beacons_out, int32_t* const* n_out, hipStream_t stream) {
+  if (policy != BKV_BEACON_FPS && policy != BKV_BEACON_INITIAL) return BKV_EINVAL;
   bkv_status st = check_shape(shape);
   if (st != BKV_OK) return st;
   if (nb_max < 1 || q_len < 0 || t_new < 0 || t_new > q_len) return BKV_EINVAL;
@@ -304,7 +313,7 @@ bkv_status bkv_update_beacons(const bkv_shape* shape, const void* const* beacons
   if (t_new > 0 && !all_set(q_new, shape->n_layers)) return BKV_EINVAL;
   const int g = shape->n_q_heads / shape->n_kv_heads;
   const long long pool_max = nb_max + static_cast<long long>(g) * t_new;
-  if (pool_max > BKV_MAX_POOL) return BKV_EUNSUPPORTED;
+  if (policy == BKV_BEACON_FPS && pool_max > BKV_MAX_POOL) return BKV_EUNSUPPORTED;
   const size_t bb = layer_bytes(shape, shape->n_kv_heads, nb_max, shape->head_dim, 2);
   const size_t qb = layer_bytes(shape, shape->n_q_heads, q_len, shape->head_dim, 2);
   const size_t cb = layer_bytes(shape, shape->n_kv_heads, 1, 1, 4);
@@ -332,7 +341,8 @@ bkv_status bkv_update_beacons(const bkv_shape* shape, const void* const* beacons
       a.beacons_out[i] = static_cast<uint16_t*>(beacons_out[l0 + i]);
       a.n_out[i] = n_out[l0 + i];
     }
-    st = hip_status(launch_fps(a, nl, shape->head_dim, static_cast<int>(pool_max), stream));
+    st = hip_status(policy == BKV_BEACON_FPS ? launch_fps(a, nl, shape->head_dim, static_cast<int>(pool_max), stream)
+                                             : launch_initial(a, nl, shape->head_dim, stream));
     if (st != BKV_OK) return st;
   }
   return BKV_OK;

@@ -93,6 +93,7 @@ hipError_t launch_qs_stats(const ScoreArgs& a, int head_dim, int grid, hipStream
 hipError_t launch_select(const SelectArgs& a, int n_layers, hipStream_t s);
 hipError_t launch_compact(const CompactArgs& a, int n_layers, int head_dim, hipStream_t s);
 hipError_t launch_fps(const FpsArgs& a, int n_layers, int head_dim, int pool_max, hipStream_t s);
+hipError_t launch_initial(const FpsArgs& a, int n_layers, int head_dim, hipStream_t s);
 
 inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
 

@@ -150,7 +150,54 @@ __global__ __launch_bounds__(kFpsThreads) void fps_kernel(const FpsArgs a) {
   if (tid == 0) a.n_out[layer][bh] = a.nb_max;
 }
 
+// Table 3's Initial+Recent baseline keeps the earliest queries instead: the live rows stay
+// in place and the new queries fill the free slots in time order (all heads of a step, in
+// head order, before the next step); once full the set never changes.  A plain copy of
+// 16-byte chunks, one workgroup per unit.
+template <int D>
+__global__ __launch_bounds__(256) void initial_kernel(const FpsArgs a) {
+  constexpr int kChunks = D / 8;
+  const int u = blockIdx.x;
+  const int per_layer = a.batch * a.n_kv_heads;
+  const int layer = u / per_layer;
+  const int bh = u - layer * per_layer;
+  const int b = bh / a.n_kv_heads;
+  const int h = bh - b * a.n_kv_heads;
+  int c_in = a.n_in[layer][bh];
+  c_in = c_in < 0 ? 0 : (c_in > a.nb_max ? a.nb_max : c_in);
+  const int fresh = a.group * a.t_new;
+  const int n = c_in + (fresh < a.nb_max - c_in ? fresh : a.nb_max - c_in);
+  const uint16_t* bin = a.beacons_in[layer] + static_cast<size_t>(bh) * a.nb_max * D;
+  uint16_t* out = a.beacons_out[layer] + static_cast<size_t>(bh) * a.nb_max * D;
+  for (int e = threadIdx.x; e < n * kChunks; e += blockDim.x) {
+    const int p = e / kChunks;
+    const int cc = e - p * kChunks;
+    const uint16_t* src;
+    if (p < c_in) {
+      src = bin + static_cast<size_t>(p) * D;
+    } else {
+      const int i = p - c_in;
+      const int t = i / a.group;
+      const int r = i - t * a.group;
+      src = a.q_new[layer] +
+            ((static_cast<size_t>(b) * a.n_q_heads + h * a.group + r) * a.q_len + (a.q_len - a.t_new + t)) * D;
+    }
+    *reinterpret_cast<uint4*>(out + static_cast<size_t>(p) * D + cc * 8) =
+        *reinterpret_cast<const uint4*>(src + cc * 8);
+  }
+  if (threadIdx.x == 0) a.n_out[layer][bh] = n;
+}
+
 }  // namespace
+
+hipError_t launch_initial(const FpsArgs& a, int n_layers, int head_dim, hipStream_t s) {
+  const unsigned grid = static_cast<unsigned>(n_layers) * a.batch * a.n_kv_heads;
+  if (head_dim == 128)
+    hipLaunchKernelGGL(initial_kernel<128>, dim3(grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(initial_kernel<64>, dim3(grid), dim3(256), 0, s, a);
+  return note_hip_error(hipGetLastError(), "initial beacons: launch");
+}
 
 hipError_t launch_fps(const FpsArgs& a, int n_layers, int head_dim, int pool_max, hipStream_t s) {
   if (pool_max > kFpsThreads) return hipErrorInvalidValue;   // rejected by the host beforehand

@@ -29,6 +29,7 @@ class EventConfig:
     budget: int         # kept keys per KV head (window included)
     t_new: int = 0      # new queries per head fed to the beacon update (0: no update)
     aggregation: str = "max"   # "max" (the method) or "mean" (Table 2's alternative)
+    beacon_policy: str = "fps"  # "fps" (continual FPS, the method) or "initial" (Table 3's Initial+Recent)
 
 
 class CompressionEvent:
@@ -63,7 +64,8 @@ class CompressionEvent:
         self.calls = {}
         if c.t_new > 0:
             self.calls["update_beacons"] = bkv.prepare_update_beacons(sh, beacons, n_beacons, c.nb_max, q, c.q_len,
-                                                                      c.t_new, self.beacons_out, self.n_beacons_out)
+                                                                      c.t_new, self.beacons_out, self.n_beacons_out,
+                                                                      c.beacon_policy)
             beacons, n_beacons = self.beacons_out, self.n_beacons_out
         self.calls["compress"] = bkv.prepare_compress(sh, k, v, q, c.q_len, c.window, beacons, n_beacons, c.nb_max,
                                                       c.budget, self.scores, self.idx, self.n_kept, self.k_out,

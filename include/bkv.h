@@ -8,6 +8,7 @@
  *   bkv_update_beacons  keeps per-KV-head beacon queries by continual farthest-point
  *                       sampling (Figure 7 caption; Abstract: compact representatives of
  *                       the global query clusters, no full query history);
+ *   bkv_update_beacons_policy  the same, or the earliest queries kept (Table 3);
  *   bkv_score           attention-based score of every cached key from the recent queries
  *                       and the beacon queries (Figure 5 (b)), max-aggregated over queries
  *                       and heads (Figure 5 (c); Table 2 caption);
@@ -128,6 +129,33 @@ bkv_status bkv_update_beacons(const bkv_shape* shape,
                               const void* const* q_new, int32_t q_len, int32_t t_new,
                               void* const* beacons_out, int32_t* const* n_out,
                               hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * Beacon update with a chosen policy.
+ * BeaconKV page, Figure 7 caption (Continual FPS) and Table 3 (the Initial+Recent
+ * baseline: the observation set is the earliest queries plus the recent ones).
+ *
+ *   BKV_BEACON_FPS:     identical to bkv_update_beacons.
+ *   BKV_BEACON_INITIAL: the live rows beacons_in[b][h][0 .. c) stay in place and the new
+ *                       queries fill the free slots in time order (for each of the t_new
+ *                       steps, the group's heads in head order) until nb_max rows are
+ *                       held; once full the set never changes.  n_out = min(nb_max,
+ *                       c + G * t_new).  No pool-size limit applies.
+ * Same arguments and errors as bkv_update_beacons, plus BKV_EINVAL for an unknown
+ * policy.
+ * ---------------------------------------------------------------------------------- */
+typedef enum {
+  BKV_BEACON_FPS = 0,     /* continual farthest-point sampling (the method) */
+  BKV_BEACON_INITIAL = 1  /* first queries kept (Table 3's Initial+Recent) */
+} bkv_beacon_policy;
+
+bkv_status bkv_update_beacons_policy(const bkv_shape* shape,
+                                     const void* const* beacons_in, const int32_t* const* n_in,
+                                     int32_t nb_max,
+                                     const void* const* q_new, int32_t q_len, int32_t t_new,
+                                     bkv_beacon_policy policy,
+                                     void* const* beacons_out, int32_t* const* n_out,
+                                     hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
  * Attention-based key scores, max-aggregated.

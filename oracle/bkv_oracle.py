@@ -218,6 +218,27 @@ def update_beacons(beacons_bits: np.ndarray, n_in: int, q_new_bits: np.ndarray,
     return pool_bits[picks], int(picks.size), picks
 
 
+def initial_beacons(beacons_bits: np.ndarray, n_in: int, q_new_bits: np.ndarray,
+                    nb_max: int) -> Tuple[np.ndarray, int]:
+    """Initial+Recent observation set (Table 3's baseline): the beacon slots hold the
+    earliest queries seen and never change once full.
+
+    Reading: "initial" queries are the first ones in time; the live rows stay in place
+    and the new queries of the group take the free slots in time order, all heads of a
+    step (head order) before the next step.  Returns (rows [n_out, D] as bit patterns,
+    n_out) with n_out = min(nb_max, n_in + G * T).
+    """
+    n_in = max(0, min(int(n_in), nb_max))
+    G, T, D = q_new_bits.shape
+    rows = [beacons_bits[p] for p in range(n_in)]
+    for t in range(T):
+        for r in range(G):
+            if len(rows) < nb_max:
+                rows.append(q_new_bits[r, t])
+    out = np.array(rows, dtype=beacons_bits.dtype).reshape(len(rows), beacons_bits.shape[1])
+    return out, len(rows)
+
+
 # ---------------------------------------------------------------------------------------------
 # One unit end to end
 # ---------------------------------------------------------------------------------------------

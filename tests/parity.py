@@ -38,9 +38,9 @@ def log(*a):
     sys.stdout.flush()
 
 
-def event_config(w: Workload, aggregation: str = "max") -> EventConfig:
+def event_config(w: Workload, aggregation: str = "max", beacon_policy: str = "fps") -> EventConfig:
     return EventConfig(w.n_layers, w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.capacity, w.q_len, w.window,
-                       w.nb_max, w.budget, w.t_new, aggregation)
+                       w.nb_max, w.budget, w.t_new, aggregation, beacon_policy)
 
 
 def build_inputs(w: Workload, device="cuda") -> Dict[str, List[torch.Tensor]]:
@@ -50,10 +50,11 @@ def build_inputs(w: Workload, device="cuda") -> Dict[str, List[torch.Tensor]]:
     return out
 
 
-def run_gpu(w: Workload, inputs=None, device="cuda", aggregation: str = "max") -> Tuple[CompressionEvent, Dict]:
+def run_gpu(w: Workload, inputs=None, device="cuda", aggregation: str = "max",
+            beacon_policy: str = "fps") -> Tuple[CompressionEvent, Dict]:
     if inputs is None:
         inputs = build_inputs(w, device)
-    ev = CompressionEvent(event_config(w, aggregation), inputs["seq_len"], device)
+    ev = CompressionEvent(event_config(w, aggregation, beacon_policy), inputs["seq_len"], device)
     ev.run(inputs["k"], inputs["v"], inputs["q"], inputs["beacons"], inputs["n_beacons"])
     torch.cuda.synchronize()
     return ev, inputs
@@ -141,9 +142,13 @@ def check_unit(w: Workload, ev: CompressionEvent, layer: int, b: int, h: int) ->
         n_out = int(ev.n_beacons_out[layer][b, h].item())
         gpu_rows = bf16_bits(ev.beacons_out[layer][b, h, :n_out])
         q_new = qb[:, w.q_len - w.t_new:, :]
-        pool_bits = O.beacon_pool(bcb, u["nb"], q_new)
-        assert n_out == min(w.nb_max, pool_bits.shape[0])
-        check_fps_replay(pool_bits, gpu_rows, w.nb_max)
+        if ev.cfg.beacon_policy == "initial":
+            want, n_want = O.initial_beacons(bcb, u["nb"], q_new, w.nb_max)
+            assert n_out == n_want and gpu_rows.tobytes() == want.tobytes(), "initial beacons differ"
+        else:
+            pool_bits = O.beacon_pool(bcb, u["nb"], q_new)
+            assert n_out == min(w.nb_max, pool_bits.shape[0])
+            check_fps_replay(pool_bits, gpu_rows, w.nb_max)
         beacons_used, nb_used = gpu_rows, n_out
     else:
         beacons_used, nb_used = bcb, u["nb"]

@@ -172,3 +172,24 @@ def test_header_aggregation_values_match_binding():
     text = open(HEADER).read()
     assert int(re.search(r"BKV_AGG_MAX = (\d+)", text).group(1)) == bkv.AGG_MAX
     assert int(re.search(r"BKV_AGG_MEAN = (\d+)", text).group(1)) == bkv.AGG_MEAN
+
+
+def test_update_beacons_policy_rejects_unknown_policy_and_keeps_fps_limits():
+    lib = bkv.load()
+    s = shape()
+
+    def call(policy, t_new=8, nb_max=16):
+        return lib.bkv_update_beacons_policy(ctypes.byref(s), arr(FAKE + (1 << 36)), arr(FAKE + (2 << 36)), nb_max,
+                                             arr(FAKE + (3 << 36)), 200, t_new, policy, arr(FAKE + (4 << 36)),
+                                             arr(FAKE + (5 << 36)), None)
+
+    assert call(2) == bkv.BKV_EINVAL
+    # continual FPS is limited to BKV_MAX_POOL candidates; 16 + 4 * 200 > 768
+    assert call(bkv.BEACON_FPS, t_new=200) == bkv.BKV_EUNSUPPORTED
+    assert call(bkv.BEACON_INITIAL, t_new=201) == bkv.BKV_EINVAL                  # t_new > q_len
+
+
+def test_header_beacon_policy_values_match_binding():
+    text = open(HEADER).read()
+    assert int(re.search(r"BKV_BEACON_FPS = (\d+)", text).group(1)) == bkv.BEACON_FPS
+    assert int(re.search(r"BKV_BEACON_INITIAL = (\d+)", text).group(1)) == bkv.BEACON_INITIAL

@@ -426,3 +426,50 @@ def test_mean_brute_force_pure_python():
     np.testing.assert_allclose(O.aggregated_scores(q, k, "mean"), want, rtol=1e-13)
     with pytest.raises(ValueError):
         O.aggregated_scores(q, k, "median")
+
+
+# ------------------------------------------------------------------------------------------------
+# Initial+Recent beacon policy (Table 3's baseline)
+# ------------------------------------------------------------------------------------------------
+
+def _rand_bits(rng, shape):
+    return rng.integers(0, 1 << 16, size=shape, dtype=np.uint16)
+
+
+def test_initial_beacons_take_earliest_queries_by_time_then_head():
+    """The new rows are the queries with the smallest (step, head) in lexicographic order."""
+    rng = np.random.default_rng(40)
+    G, T, D, nb_max = 3, 5, 4, 9
+    old = _rand_bits(rng, (nb_max, D))
+    q = _rand_bits(rng, (G, T, D))
+    for n_in in (0, 2, 9):
+        rows, n = O.initial_beacons(old, n_in, q, nb_max)
+        assert n == min(nb_max, n_in + G * T)
+        assert rows[:n_in].tobytes() == old[:n_in].tobytes()
+        heads, steps = np.meshgrid(np.arange(G), np.arange(T), indexing="ij")
+        order = np.lexsort((heads.ravel(), steps.ravel()))[: n - n_in]   # by step, then head
+        want = q.reshape(G * T, D)[order]
+        assert rows[n_in:].tobytes() == want.tobytes()
+
+
+def test_initial_beacons_frozen_once_full():
+    rng = np.random.default_rng(41)
+    G, T, D, nb_max = 4, 8, 6, 16
+    old = _rand_bits(rng, (nb_max, D))
+    rows, n = O.initial_beacons(old, 0, _rand_bits(rng, (G, T, D)), nb_max)
+    assert n == nb_max
+    again, n2 = O.initial_beacons(rows, n, _rand_bits(rng, (G, T, D)), nb_max)
+    assert n2 == nb_max and again.tobytes() == rows.tobytes()
+
+
+def test_initial_and_fps_keep_the_same_set_when_everything_fits():
+    """With no more candidates than slots both policies keep every candidate (FPS in pool
+    order, the initial policy in time order): the same set of rows."""
+    rng = np.random.default_rng(42)
+    G, T, D, nb_max = 2, 3, 8, 10
+    old = _rand_bits(rng, (nb_max, D)) & 0x3FFF        # finite, non-zero bf16 patterns
+    q = (_rand_bits(rng, (G, T, D)) & 0x3FFF) | 0x0080
+    a, na = O.initial_beacons(old, 3, q, nb_max)
+    b, nb, _ = O.update_beacons(old, 3, q, nb_max)
+    assert na == nb == 3 + G * T
+    assert sorted(r.tobytes() for r in a) == sorted(r.tobytes() for r in b)

@@ -10,10 +10,11 @@ from parity import all_units, check_units, log, run_gpu
 pytestmark = pytest.mark.gpu
 
 
-def _run_all(w, aggregation="max"):
+def _run_all(w, aggregation="max", beacon_policy="fps"):
     log(f"[parity] {w.name}: layers {w.n_layers} batch {w.batch} cap {w.capacity} window {w.window} "
-        f"nb {w.nb_init}/{w.nb_max} budget {w.budget} t_new {w.t_new} aggregation {aggregation}")
-    ev, _ = run_gpu(w, aggregation=aggregation)
+        f"nb {w.nb_init}/{w.nb_max} budget {w.budget} t_new {w.t_new} aggregation {aggregation} "
+        f"beacons {beacon_policy}")
+    ev, _ = run_gpu(w, aggregation=aggregation, beacon_policy=beacon_policy)
     worst = check_units(w, ev, all_units(w))
     log(f"[parity] {w.name}: worst {worst}")
     return worst
@@ -113,3 +114,19 @@ def test_recent_beacon_splits(n_recent, n_beacon):
                                             ragged=(700, 2048), budget=512, window=n_recent, nb_init=n_beacon,
                                             nb_max=n_beacon)
     _run_all(w)
+
+
+# Table 3's Initial+Recent: the beacon slots keep the earliest queries (filled in time
+# order, frozen once full), scored with the recent window as usual.
+INITIAL_CASES = {
+    "tiny": WORKLOADS["tiny"],                                   # 4 live rows, slots full: frozen
+    "empty_start": EDGE["fps_empty_beacons"],                    # no live rows: filled from new queries
+    "partial_fill": EDGE["fps_small_pool"],                      # 2 live of 32 slots, pool smaller than slots
+    "serving": WORKLOADS["qwen4b_serving"].replace(n_layers=1, batch=3, capacity=2048, ragged=(700, 2048),
+                                                   budget=400, nb_init=5, t_new=3),
+}
+
+
+@pytest.mark.parametrize("case", sorted(INITIAL_CASES))
+def test_initial_recent_beacons(case):
+    _run_all(INITIAL_CASES[case].replace(name="initial_" + case), beacon_policy="initial")
