@@ -37,6 +37,7 @@ MAX_POOL = 768
 EXPORTS = ["bkv_status_string", "bkv_version", "bkv_last_error", "bkv_update_beacons", "bkv_update_beacons_policy",
            "bkv_score_workspace_bytes",
            "bkv_score", "bkv_score_agg", "bkv_select_workspace_bytes", "bkv_select_topk", "bkv_compact",
+           "bkv_compact_into",
            "bkv_compress_workspace_bytes", "bkv_compress"]
 
 
@@ -91,6 +92,8 @@ def load() -> ctypes.CDLL:
     lib.bkv_select_topk.argtypes = [P(_Shape), arr, i32, i32, arr, arr, vp, sz, vp]
     lib.bkv_compact.restype = ctypes.c_int
     lib.bkv_compact.argtypes = [P(_Shape), arr, arr, arr, arr, i32, arr, arr, vp]
+    lib.bkv_compact_into.restype = ctypes.c_int
+    lib.bkv_compact_into.argtypes = [P(_Shape), arr, arr, arr, arr, i32, i32, arr, arr, vp]
     lib.bkv_compress_workspace_bytes.restype = sz
     lib.bkv_compress_workspace_bytes.argtypes = [P(_Shape), i32, i32, i32]
     lib.bkv_compress.restype = ctypes.c_int
@@ -278,23 +281,31 @@ def select_topk(s: CacheShape, scores, budget: int, window: int, idx, n_kept, st
     prepare_select_topk(s, scores, budget, window, idx, n_kept)(stream)
 
 
-def prepare_compact(s: CacheShape, k, v, idx, n_kept, budget: int, k_out, v_out) -> Call:
+def prepare_compact(s: CacheShape, k, v, idx, n_kept, budget: int, k_out, v_out,
+                    out_capacity: Optional[int] = None) -> Call:
+    """bkv_compact (outputs [B][Hkv][budget][D]) or, with out_capacity, bkv_compact_into
+    (outputs [B][Hkv][out_capacity][D], kept rows first)."""
     lib = load()
     B, Hkv, D, cap, n = s.batch, s.n_kv_heads, s.head_dim, s.capacity, s.n_layers
     shape = s.c()
+    rows = budget if out_capacity is None else out_capacity
     kp = _layers(k, n, torch.bfloat16, (B, Hkv, cap, D), "k")
     vp = _layers(v, n, torch.bfloat16, (B, Hkv, cap, D), "v")
     ip = _layers(idx, n, torch.int32, (B, Hkv, budget), "idx")
     np_ = _layers(n_kept, n, torch.int32, (B, Hkv), "n_kept")
-    ko = _layers(k_out, n, torch.bfloat16, (B, Hkv, budget, D), "k_out")
-    vo = _layers(v_out, n, torch.bfloat16, (B, Hkv, budget, D), "v_out")
-    args = (ctypes.byref(shape), kp, vp, ip, np_, budget, ko, vo)
-    return Call(lib.bkv_compact, args, "bkv_compact", (shape, s.seq_len, k, v, idx, n_kept, k_out, v_out))
+    ko = _layers(k_out, n, torch.bfloat16, (B, Hkv, rows, D), "k_out")
+    vo = _layers(v_out, n, torch.bfloat16, (B, Hkv, rows, D), "v_out")
+    keep = (shape, s.seq_len, k, v, idx, n_kept, k_out, v_out)
+    if out_capacity is None:
+        return Call(lib.bkv_compact, (ctypes.byref(shape), kp, vp, ip, np_, budget, ko, vo), "bkv_compact", keep)
+    args = (ctypes.byref(shape), kp, vp, ip, np_, budget, out_capacity, ko, vo)
+    return Call(lib.bkv_compact_into, args, "bkv_compact_into", keep)
 
 
-def compact(s: CacheShape, k, v, idx, n_kept, budget: int, k_out, v_out, stream=None) -> None:
-    """Gather the kept K/V rows into compacted caches (bkv_compact)."""
-    prepare_compact(s, k, v, idx, n_kept, budget, k_out, v_out)(stream)
+def compact(s: CacheShape, k, v, idx, n_kept, budget: int, k_out, v_out, stream=None,
+            out_capacity: Optional[int] = None) -> None:
+    """Gather the kept K/V rows into compacted caches (bkv_compact / bkv_compact_into)."""
+    prepare_compact(s, k, v, idx, n_kept, budget, k_out, v_out, out_capacity)(stream)
 
 
 def compress_workspace_bytes(s: CacheShape, window: int, nb_max: int, budget: int) -> int:

@@ -125,15 +125,15 @@ bkv_status check_select_args(const bkv_shape* s, const float* const* scores, int
 
 bkv_status check_compact_args(const bkv_shape* s, const void* const* k, const void* const* v,
                               const int32_t* const* idx, const int32_t* const* n_kept, int32_t budget,
-                              void* const* k_out, void* const* v_out) {
+                              int32_t out_capacity, void* const* k_out, void* const* v_out) {
   bkv_status st = check_shape(s);
   if (st != BKV_OK) return st;
-  if (budget < 1) return BKV_EINVAL;
+  if (budget < 1 || out_capacity < budget) return BKV_EINVAL;
   if (!all_set(k, s->n_layers) || !all_set(v, s->n_layers) || !all_set(idx, s->n_layers) ||
       !all_set(n_kept, s->n_layers) || !all_set(k_out, s->n_layers) || !all_set(v_out, s->n_layers))
     return BKV_EINVAL;
   const size_t kb = layer_bytes(s, s->n_kv_heads, s->capacity, s->head_dim, 2);
-  const size_t ob = layer_bytes(s, s->n_kv_heads, budget, s->head_dim, 2);
+  const size_t ob = layer_bytes(s, s->n_kv_heads, out_capacity, s->head_dim, 2);
   if (kb == SIZE_MAX || ob == SIZE_MAX) return BKV_EINVAL;
   for (int l = 0; l < s->n_layers; ++l) {
     if (overlap(k_out[l], ob, k[l], kb) || overlap(k_out[l], ob, v[l], kb) || overlap(v_out[l], ob, k[l], kb) ||
@@ -268,7 +268,13 @@ bkv_status bkv_select_topk(const bkv_shape* shape, const float* const* scores, i
 bkv_status bkv_compact(const bkv_shape* shape, const void* const* k, const void* const* v,
                        const int32_t* const* idx, const int32_t* const* n_kept, int32_t budget, void* const* k_out,
                        void* const* v_out, hipStream_t stream) {
-  bkv_status st = check_compact_args(shape, k, v, idx, n_kept, budget, k_out, v_out);
+  return bkv_compact_into(shape, k, v, idx, n_kept, budget, budget, k_out, v_out, stream);
+}
+
+bkv_status bkv_compact_into(const bkv_shape* shape, const void* const* k, const void* const* v,
+                            const int32_t* const* idx, const int32_t* const* n_kept, int32_t budget,
+                            int32_t out_capacity, void* const* k_out, void* const* v_out, hipStream_t stream) {
+  bkv_status st = check_compact_args(shape, k, v, idx, n_kept, budget, out_capacity, k_out, v_out);
   if (st != BKV_OK) return st;
   CompactArgs a;
   memset(&a, 0, sizeof(a));
@@ -276,6 +282,7 @@ bkv_status bkv_compact(const bkv_shape* shape, const void* const* k, const void*
   a.n_kv_heads = shape->n_kv_heads;
   a.capacity = shape->capacity;
   a.budget = budget;
+  a.out_capacity = out_capacity;
   for (int l0 = 0; l0 < shape->n_layers; l0 += kMaxLayers) {
     const int nl = std::min(kMaxLayers, shape->n_layers - l0);
     for (int i = 0; i < nl; ++i) {
@@ -360,7 +367,7 @@ bkv_status bkv_compress(const bkv_shape* shape, const void* const* k, const void
                         size_t workspace_bytes, hipStream_t stream) {
   bkv_status st = check_score_args(shape, k, q, q_len, window, beacons, n_beacons, nb_max, scores);
   if (st == BKV_OK) st = check_select_args(shape, scores, budget, window, idx, n_kept);
-  if (st == BKV_OK) st = check_compact_args(shape, k, v, idx, n_kept, budget, k_out, v_out);
+  if (st == BKV_OK) st = check_compact_args(shape, k, v, idx, n_kept, budget, budget, k_out, v_out);
   if (st != BKV_OK) return st;
   st = bkv_score(shape, k, q, q_len, window, beacons, n_beacons, nb_max, scores, workspace, workspace_bytes, stream);
   if (st != BKV_OK) return st;

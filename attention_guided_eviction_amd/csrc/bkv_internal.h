@@ -68,6 +68,7 @@ struct CompactArgs {
   uint16_t* k_out[kMaxLayers];
   uint16_t* v_out[kMaxLayers];
   int batch, n_kv_heads, capacity, budget;
+  int out_capacity;     // rows per (sequence, KV head) of k_out / v_out (>= budget)
 };
 
 // ---- beacons -----------------------------------------------------------------------------

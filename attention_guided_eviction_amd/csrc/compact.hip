@@ -27,7 +27,7 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(const CompactArgs a, 
   int src = a.idx[layer][static_cast<size_t>(bh) * a.budget + r];
   src = src < 0 ? 0 : (src >= a.capacity ? a.capacity - 1 : src);
   const size_t in_off = (static_cast<size_t>(bh) * a.capacity + src) * D + part * 8;
-  const size_t out_off = (static_cast<size_t>(bh) * a.budget + r) * D + part * 8;
+  const size_t out_off = (static_cast<size_t>(bh) * a.out_capacity + r) * D + part * 8;
   const uint4 kv = *reinterpret_cast<const uint4*>(a.k[layer] + in_off);
   const uint4 vv = *reinterpret_cast<const uint4*>(a.v[layer] + in_off);
   *reinterpret_cast<uint4*>(a.k_out[layer] + out_off) = kv;

@@ -17,6 +17,7 @@
  *                       always kept;
  *   bkv_compact         eviction: the kept K/V rows gathered into a compacted cache
  *                       (Abstract);
+ *   bkv_compact_into    the same into a cache with room for the next decoded tokens;
  *   bkv_compress        bkv_score + bkv_select_topk + bkv_compact in one call.
  *
  * Conventions shared by every entry point
@@ -255,6 +256,25 @@ bkv_status bkv_compact(const bkv_shape* shape,
                        const int32_t* const* idx, const int32_t* const* n_kept, int32_t budget,
                        void* const* k_out, void* const* v_out,
                        hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * Compaction into a cache with room to grow.
+ * BeaconKV page, Abstract (the cache keeps only the selected KV pairs) and the serving
+ * setting of Table 4 (decoding continues after each compression).
+ *
+ * As bkv_compact, but k_out / v_out are laid out [batch][n_kv_heads][out_capacity]
+ * [head_dim] (out_capacity >= budget): the kept rows land in rows 0 .. n-1 of each
+ * (sequence, KV head) and rows from n up are left untouched, so a caller can append the
+ * next decoded tokens after them and compress again from that buffer (double buffering:
+ * the outputs must not overlap K or V).  bkv_compact is the case out_capacity = budget.
+ * Errors: as bkv_compact, plus BKV_EINVAL if out_capacity < budget.
+ * ---------------------------------------------------------------------------------- */
+bkv_status bkv_compact_into(const bkv_shape* shape,
+                            const void* const* k, const void* const* v,
+                            const int32_t* const* idx, const int32_t* const* n_kept, int32_t budget,
+                            int32_t out_capacity,
+                            void* const* k_out, void* const* v_out,
+                            hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
  * One compression event: bkv_score, then bkv_select_topk, then bkv_compact, with the

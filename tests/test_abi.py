@@ -193,3 +193,18 @@ def test_header_beacon_policy_values_match_binding():
     text = open(HEADER).read()
     assert int(re.search(r"BKV_BEACON_FPS = (\d+)", text).group(1)) == bkv.BEACON_FPS
     assert int(re.search(r"BKV_BEACON_INITIAL = (\d+)", text).group(1)) == bkv.BEACON_INITIAL
+
+
+def test_compact_into_validates_out_capacity():
+    lib = bkv.load()
+    s = shape()
+    ks, vs = arr(FAKE + (1 << 36)), arr(FAKE + (2 << 36))
+
+    def call(budget, out_cap, k_out=None):
+        return lib.bkv_compact_into(ctypes.byref(s), ks, vs, arr(FAKE + (3 << 36)), arr(FAKE + (4 << 36)), budget,
+                                    out_cap, k_out or arr(FAKE + (5 << 36)), arr(FAKE + (6 << 36)), None)
+
+    assert call(64, 63) == bkv.BKV_EINVAL
+    assert call(0, 64) == bkv.BKV_EINVAL
+    # an output laid out with 2048 rows per (sequence, KV head) reaches into K here
+    assert call(64, 2048, k_out=arr(FAKE + (1 << 36) - 2 * 2 * 2048 * 128 * 2 + 4096)) == bkv.BKV_EALIAS
