@@ -37,7 +37,7 @@ MAX_POOL = 768
 EXPORTS = ["bkv_status_string", "bkv_version", "bkv_last_error", "bkv_update_beacons", "bkv_update_beacons_policy",
            "bkv_score_workspace_bytes",
            "bkv_score", "bkv_score_agg", "bkv_select_workspace_bytes", "bkv_select_topk", "bkv_compact",
-           "bkv_compact_into",
+           "bkv_compact_into", "bkv_decode_workspace_bytes", "bkv_decode_attention",
            "bkv_compress_workspace_bytes", "bkv_compress"]
 
 
@@ -92,6 +92,10 @@ def load() -> ctypes.CDLL:
     lib.bkv_select_topk.argtypes = [P(_Shape), arr, i32, i32, arr, arr, vp, sz, vp]
     lib.bkv_compact.restype = ctypes.c_int
     lib.bkv_compact.argtypes = [P(_Shape), arr, arr, arr, arr, i32, arr, arr, vp]
+    lib.bkv_decode_workspace_bytes.restype = sz
+    lib.bkv_decode_workspace_bytes.argtypes = [P(_Shape)]
+    lib.bkv_decode_attention.restype = ctypes.c_int
+    lib.bkv_decode_attention.argtypes = [P(_Shape), arr, arr, arr, arr, vp, sz, vp]
     lib.bkv_compact_into.restype = ctypes.c_int
     lib.bkv_compact_into.argtypes = [P(_Shape), arr, arr, arr, arr, i32, i32, arr, arr, vp]
     lib.bkv_compress_workspace_bytes.restype = sz
@@ -306,6 +310,29 @@ def compact(s: CacheShape, k, v, idx, n_kept, budget: int, k_out, v_out, stream=
             out_capacity: Optional[int] = None) -> None:
     """Gather the kept K/V rows into compacted caches (bkv_compact / bkv_compact_into)."""
     prepare_compact(s, k, v, idx, n_kept, budget, k_out, v_out, out_capacity)(stream)
+
+
+def decode_workspace_bytes(s: CacheShape) -> int:
+    return int(load().bkv_decode_workspace_bytes(ctypes.byref(s.c())))
+
+
+def prepare_decode_attention(s: CacheShape, q, k, v, out, workspace: Optional[torch.Tensor]) -> Call:
+    """One decoding step of attention over a cache (bkv_decode_attention): q per layer
+    bf16 [B][Hq][D], k and v [B][Hkv][capacity][D], out fp32 [B][Hq][D]."""
+    lib = load()
+    B, Hq, Hkv, D, cap, n = s.batch, s.n_q_heads, s.n_kv_heads, s.head_dim, s.capacity, s.n_layers
+    shape = s.c()
+    qp = _layers(q, n, torch.bfloat16, (B, Hq, D), "q")
+    kp = _layers(k, n, torch.bfloat16, (B, Hkv, cap, D), "k")
+    vp = _layers(v, n, torch.bfloat16, (B, Hkv, cap, D), "v")
+    op = _layers(out, n, torch.float32, (B, Hq, D), "out")
+    wp, wn = _workspace(workspace, int(lib.bkv_decode_workspace_bytes(ctypes.byref(shape))))
+    args = (ctypes.byref(shape), qp, kp, vp, op, wp, wn)
+    return Call(lib.bkv_decode_attention, args, "bkv_decode_attention", (shape, s.seq_len, q, k, v, out, workspace))
+
+
+def decode_attention(s: CacheShape, q, k, v, out, workspace: Optional[torch.Tensor], stream=None) -> None:
+    prepare_decode_attention(s, q, k, v, out, workspace)(stream)
 
 
 def compress_workspace_bytes(s: CacheShape, window: int, nb_max: int, budget: int) -> int:

@@ -145,6 +145,23 @@ bkv_status check_compact_args(const bkv_shape* s, const void* const* k, const vo
 
 bkv_status hip_status(hipError_t e) { return e == hipSuccess ? BKV_OK : BKV_EHIP; }
 
+struct DecodeWs {
+  size_t m_bytes, o_bytes, total;
+  int chunks;
+};
+
+// Partials of the largest launch (kMaxLayers layers or all of them).
+DecodeWs decode_ws(const bkv_shape* s) {
+  DecodeWs w{};
+  w.chunks = (s->capacity + kDecodeChunk - 1) / kDecodeChunk;
+  const size_t cells = static_cast<size_t>(std::min(s->n_layers, kMaxLayers)) * s->batch * s->n_kv_heads *
+                       kDecodeMaxGroup * w.chunks;
+  w.m_bytes = align_up(cells * sizeof(float));
+  w.o_bytes = align_up(cells * static_cast<size_t>(s->head_dim) * sizeof(float));
+  w.total = 2 * w.m_bytes + w.o_bytes;
+  return w;
+}
+
 thread_local char g_last_error[256] = "no HIP error recorded";
 
 }  // namespace
@@ -374,6 +391,61 @@ bkv_status bkv_compress(const bkv_shape* shape, const void* const* k, const void
   st = bkv_select_topk(shape, scores, budget, window, idx, n_kept, nullptr, 0, stream);
   if (st != BKV_OK) return st;
   return bkv_compact(shape, k, v, idx, n_kept, budget, k_out, v_out, stream);
+}
+
+size_t bkv_decode_workspace_bytes(const bkv_shape* shape) {
+  if (check_shape(shape) != BKV_OK || shape->n_q_heads / shape->n_kv_heads > kDecodeMaxGroup) return 0;
+  return decode_ws(shape).total;
+}
+
+bkv_status bkv_decode_attention(const bkv_shape* shape, const void* const* q, const void* const* k,
+                                const void* const* v, float* const* out, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  bkv_status st = check_shape(shape);
+  if (st != BKV_OK) return st;
+  const int g = shape->n_q_heads / shape->n_kv_heads;
+  if (g > kDecodeMaxGroup) return BKV_EUNSUPPORTED;
+  if (!all_set(q, shape->n_layers) || !all_set(k, shape->n_layers) || !all_set(v, shape->n_layers) ||
+      !all_set(out, shape->n_layers))
+    return BKV_EINVAL;
+  const DecodeWs ws = decode_ws(shape);
+  if (workspace == nullptr || workspace_bytes < ws.total || reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
+    return BKV_EWORKSPACE;
+  const size_t qb = layer_bytes(shape, shape->n_q_heads, 1, shape->head_dim, 2);
+  const size_t ob = layer_bytes(shape, shape->n_q_heads, 1, shape->head_dim, 4);
+  const size_t kb = layer_bytes(shape, shape->n_kv_heads, shape->capacity, shape->head_dim, 2);
+  if (qb == SIZE_MAX || ob == SIZE_MAX || kb == SIZE_MAX) return BKV_EINVAL;
+  for (int l = 0; l < shape->n_layers; ++l) {
+    if (overlap(out[l], ob, q[l], qb) || overlap(out[l], ob, k[l], kb) || overlap(out[l], ob, v[l], kb) ||
+        overlap(out[l], ob, workspace, ws.total))
+      return BKV_EALIAS;
+  }
+  DecodeArgs a;
+  memset(&a, 0, sizeof(a));
+  char* wsp = static_cast<char*>(workspace);
+  a.part_m = reinterpret_cast<float*>(wsp);
+  a.part_z = reinterpret_cast<float*>(wsp + ws.m_bytes);
+  a.part_o = reinterpret_cast<float*>(wsp + 2 * ws.m_bytes);
+  a.seq_len = shape->seq_len;
+  a.batch = shape->batch;
+  a.n_q_heads = shape->n_q_heads;
+  a.n_kv_heads = shape->n_kv_heads;
+  a.group = g;
+  a.capacity = shape->capacity;
+  a.chunks = ws.chunks;
+  a.scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(shape->head_dim)));
+  for (int l0 = 0; l0 < shape->n_layers; l0 += kMaxLayers) {
+    const int nl = std::min(kMaxLayers, shape->n_layers - l0);
+    for (int i = 0; i < nl; ++i) {
+      a.q[i] = static_cast<const uint16_t*>(q[l0 + i]);
+      a.k[i] = static_cast<const uint16_t*>(k[l0 + i]);
+      a.v[i] = static_cast<const uint16_t*>(v[l0 + i]);
+      a.out[i] = out[l0 + i];
+    }
+    st = hip_status(launch_decode(a, nl, shape->head_dim, stream));
+    if (st != BKV_OK) return st;
+  }
+  return BKV_OK;
 }
 
 }  // extern "C"

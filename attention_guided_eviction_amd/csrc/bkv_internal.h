@@ -83,6 +83,25 @@ struct FpsArgs {
   int batch, n_q_heads, n_kv_heads, group, nb_max, q_len, t_new;
 };
 
+// ---- decode attention ----------------------------------------------------------------------
+
+constexpr int kDecodeChunk = 1024;     // keys per workgroup (4 waves x 256)
+constexpr int kDecodeMaxGroup = 8;     // query heads per KV head
+
+struct DecodeArgs {
+  const uint16_t* q[kMaxLayers];     // [batch][n_q_heads][head_dim]
+  const uint16_t* k[kMaxLayers];     // [batch][n_kv_heads][capacity][head_dim]
+  const uint16_t* v[kMaxLayers];
+  float* out[kMaxLayers];            // [batch][n_q_heads][head_dim]
+  const int32_t* seq_len;
+  float* part_m;                     // [unit][kDecodeMaxGroup][chunks] running max (log2 domain)
+  float* part_z;                     // same cells: sum of exp2(t - m)
+  float* part_o;                     // [cell][head_dim] unnormalised output
+  int batch, n_q_heads, n_kv_heads, group, capacity;
+  int chunks;                        // ceil(capacity / kDecodeChunk)
+  float scale_log2;
+};
+
 // Launchers (return hipSuccess or the launch error).  n_layers <= kMaxLayers.
 hipError_t launch_score(const ScoreArgs& a, int n_layers, int head_dim, hipStream_t s);
 // Statistics pass with the observation rows in registers, for units of at most kQsMaxRows
@@ -93,6 +112,7 @@ hipError_t qs_stats_occupancy(int head_dim, int obs_pad, int* per_cu);
 hipError_t launch_qs_stats(const ScoreArgs& a, int head_dim, int grid, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, int n_layers, hipStream_t s);
 hipError_t launch_compact(const CompactArgs& a, int n_layers, int head_dim, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, int n_layers, int head_dim, hipStream_t s);
 hipError_t launch_fps(const FpsArgs& a, int n_layers, int head_dim, int pool_max, hipStream_t s);
 hipError_t launch_initial(const FpsArgs& a, int n_layers, int head_dim, hipStream_t s);
 

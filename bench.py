@@ -50,6 +50,8 @@ def parse():
     p.add_argument("--steady-state", type=int, default=0, metavar="CYCLES",
                    help="time CYCLES steady-state cycles (append a chunk of t_new tokens, refresh beacons, compress "
                         "back to the budget) instead of one event")
+    p.add_argument("--decode", action="store_true",
+                   help="time one decoding step of attention over the full caches and over the compacted ones")
     p.add_argument("--quiet", action="store_true")
     return p.parse_args()
 
@@ -172,6 +174,53 @@ def cpu_baseline(w, n_units, budget_s=15.0):
                       f"(beacon update, scores, top-K, compaction); rows/s divided by layers x KV heads"}
 
 
+def decode_bench(args, w, log):
+    """Decode attention (one new query per head, all layers) over the workload's full caches
+    and over the caches one compression event leaves, HIP events around each."""
+    import torch
+    from synth import layer_tensors, seq_lengths
+    from attention_guided_eviction_amd import bkv
+    from attention_guided_eviction_amd.event import CompressionEvent, EventConfig
+    dev = torch.device("cuda:0")
+    layers = [layer_tensors(w, l, dev) for l in range(w.n_layers)]
+    inp = {key: [lt[key] for lt in layers] for key in layers[0]}
+    del layers
+    lens = seq_lengths(w)
+    seq = torch.from_numpy(lens).to(dev)
+    cfg = EventConfig(w.n_layers, w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.capacity, w.q_len, w.window,
+                      w.nb_max, w.budget, w.t_new)
+    ev = CompressionEvent(cfg, seq, dev)
+    ev.run(inp["k"], inp["v"], inp["q"], inp["beacons"], inp["n_beacons"])
+    q = [t[:, :, -1].contiguous() for t in inp["q"]]
+    out = [torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device=dev) for _ in q]
+    kept = torch.clamp(seq, max=w.budget)
+    res = {}
+    for name, k, v, cap, sl, n_rows in (("full", inp["k"], inp["v"], w.capacity, seq, lens.sum()),
+                                        ("compacted", ev.k_out, ev.v_out, w.budget, kept,
+                                         sum(min(int(x), w.budget) for x in lens))):
+        shape = bkv.CacheShape(w.n_layers, w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, cap, sl)
+        ws = bkv.alloc_workspace(bkv.decode_workspace_bytes(shape), dev)
+        call = bkv.prepare_decode_attention(shape, q, k, v, out, ws)
+        for _ in range(args.warmup):
+            call()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(args.steps):
+            call()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / args.steps
+        nbytes = float(n_rows) * w.n_layers * w.n_kv_heads * w.head_dim * 2 * 2
+        res[name] = {"ms_per_step": round(ms, 4), "cached_rows": int(n_rows), "alg_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "alg_frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"[bench] decode over {name} caches: {ms:.3f} ms per step")
+    out_line = {"metric": "decode attention over the full vs the compacted cache (one step, all layers)",
+                "workload": w.name, "budget": w.budget, "results": res,
+                "speedup_from_compression": round(res["full"]["ms_per_step"] / res["compacted"]["ms_per_step"], 2)}
+    print(json.dumps(out_line), flush=True)
+
+
 def steady_state(args, w, log):
     """Steady-state cycles of the workload's geometry: every sequence at the budget, a chunk
     of t_new tokens appended, beacons refreshed, the cache compressed back to the budget."""
@@ -243,6 +292,8 @@ def main():
     w = WORKLOADS[args.workload]
     if args.steady_state > 0:
         return steady_state(args, w, log)
+    if args.decode:
+        return decode_bench(args, w, log)
     if args.window is not None:
         w = w.replace(window=args.window)
     if args.beacons is not None:

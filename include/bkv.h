@@ -18,7 +18,8 @@
  *   bkv_compact         eviction: the kept K/V rows gathered into a compacted cache
  *                       (Abstract);
  *   bkv_compact_into    the same into a cache with room for the next decoded tokens;
- *   bkv_compress        bkv_score + bkv_select_topk + bkv_compact in one call.
+ *   bkv_compress        bkv_score + bkv_select_topk + bkv_compact in one call;
+ *   bkv_decode_attention  one decoding step of attention over the (compacted) cache.
  *
  * Conventions shared by every entry point
  * ----------------------------------------
@@ -294,6 +295,32 @@ bkv_status bkv_compress(const bkv_shape* shape,
                         void* const* k_out, void* const* v_out,
                         void* workspace, size_t workspace_bytes,
                         hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * One decoding step of attention over a cache (typically the compacted one).
+ * BeaconKV page, Abstract and Table 4: after compression decoding attends over the kept
+ * KV pairs only, which is where the method's memory and throughput gains come from.
+ *
+ * For every sequence b and query head hq (KV head h = hq / G):
+ *     out[b][hq] = sum_j w_j v[b][h][j],  w = softmax_j(q[b][hq] . k[b][h][j] / sqrt(d))
+ * over the valid rows j < L_b (fp32 accumulation; out = 0 when L_b = 0).
+ *
+ * q:    per layer bf16 [batch][n_q_heads][head_dim] (one new query per head).
+ * k, v: per layer bf16 [batch][n_kv_heads][capacity][head_dim] (e.g. bkv_compact_into's
+ *       output with capacity = its out_capacity and seq_len = the kept counts).
+ * out:  per layer fp32 [batch][n_q_heads][head_dim].
+ * workspace: at least bkv_decode_workspace_bytes(shape) bytes, 256-byte aligned.
+ * Errors: BKV_EINVAL, BKV_EUNSUPPORTED (head_dim; more than 8 query heads per KV head),
+ *         BKV_EWORKSPACE, BKV_EALIAS if an out layer overlaps q, k, v or the workspace.
+ * ---------------------------------------------------------------------------------- */
+size_t bkv_decode_workspace_bytes(const bkv_shape* shape);
+
+bkv_status bkv_decode_attention(const bkv_shape* shape,
+                                const void* const* q,
+                                const void* const* k, const void* const* v,
+                                float* const* out,
+                                void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
 
 #ifdef __cplusplus
 }  /* extern "C" */

@@ -240,6 +240,20 @@ def initial_beacons(beacons_bits: np.ndarray, n_in: int, q_new_bits: np.ndarray,
 
 
 # ---------------------------------------------------------------------------------------------
+# Decoding over the (compacted) cache (Abstract; Table 4)
+# ---------------------------------------------------------------------------------------------
+
+def decode_attention(q: np.ndarray, keys: np.ndarray, values: np.ndarray) -> np.ndarray:
+    """One decoding step of attention for the query heads of one KV head: [n_q, D] outputs,
+    each the softmax(q.k / sqrt(d))-weighted sum of the value rows.  With no rows the
+    output is 0.  The compressed cache exists to be read this way: decoding attends over
+    the kept KV pairs only."""
+    if keys.shape[0] == 0:
+        return np.zeros((q.shape[0], values.shape[1]))
+    return attention_probabilities(q, keys) @ values
+
+
+# ---------------------------------------------------------------------------------------------
 # One unit end to end
 # ---------------------------------------------------------------------------------------------
 

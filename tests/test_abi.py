@@ -208,3 +208,22 @@ def test_compact_into_validates_out_capacity():
     assert call(0, 64) == bkv.BKV_EINVAL
     # an output laid out with 2048 rows per (sequence, KV head) reaches into K here
     assert call(64, 2048, k_out=arr(FAKE + (1 << 36) - 2 * 2 * 2048 * 128 * 2 + 4096)) == bkv.BKV_EALIAS
+
+
+def test_decode_attention_validation():
+    lib = bkv.load()
+    qs, ks, vs, os_ = arr(FAKE + (1 << 36)), arr(FAKE + (2 << 36)), arr(FAKE + (3 << 36)), arr(FAKE + (4 << 36))
+    s = shape()
+    need = lib.bkv_decode_workspace_bytes(ctypes.byref(s))
+    assert need > 0
+    ws = FAKE + (1 << 40)
+
+    def call(s=s, q=qs, out=os_, ws=ws, nbytes=need):
+        return lib.bkv_decode_attention(ctypes.byref(s), q, ks, vs, out, ws, nbytes, None)
+
+    assert call(s=shape(n_q_heads=18, n_kv_heads=2)) == bkv.BKV_EUNSUPPORTED     # 9 query heads per KV head
+    assert lib.bkv_decode_workspace_bytes(ctypes.byref(shape(n_q_heads=18, n_kv_heads=2))) == 0
+    assert call(q=nulls()) == bkv.BKV_EINVAL
+    assert call(nbytes=need - 1) == bkv.BKV_EWORKSPACE
+    assert call(ws=ws + 8) == bkv.BKV_EWORKSPACE
+    assert call(out=arr(FAKE + (2 << 36) + 512)) == bkv.BKV_EALIAS                # out inside K

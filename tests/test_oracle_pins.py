@@ -473,3 +473,44 @@ def test_initial_and_fps_keep_the_same_set_when_everything_fits():
     b, nb, _ = O.update_beacons(old, 3, q, nb_max)
     assert na == nb == 3 + G * T
     assert sorted(r.tobytes() for r in a) == sorted(r.tobytes() for r in b)
+
+
+# ------------------------------------------------------------------------------------------------
+# decoding over the compacted cache
+# ------------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n_q,L,d", [(1, 5, 8), (4, 300, 64), (7, 1000, 128)])
+def test_decode_attention_equals_torch_sdpa(n_q, L, d):
+    rng = np.random.default_rng(n_q * 31 + L)
+    q = rng.standard_normal((n_q, d)) * 1.5
+    k = rng.standard_normal((L, d))
+    v = rng.standard_normal((L, d))
+    ref = torch.nn.functional.scaled_dot_product_attention(torch.from_numpy(q)[None], torch.from_numpy(k)[None],
+                                                           torch.from_numpy(v)[None])[0]
+    np.testing.assert_allclose(O.decode_attention(q, k, v), ref.numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_decode_attention_special_cases():
+    rng = np.random.default_rng(50)
+    d = 16
+    v = rng.standard_normal((9, d))
+    k_same = np.repeat(rng.standard_normal((1, d)), 9, axis=0)
+    q = rng.standard_normal((3, d))
+    np.testing.assert_allclose(O.decode_attention(q, k_same, v), np.repeat(v.mean(0, keepdims=True), 3, 0),
+                               rtol=1e-13, atol=1e-14)          # equal keys: plain mean of the values
+    k = rng.standard_normal((9, d)) * 0.01
+    k[4] = 60.0 * q[0]
+    np.testing.assert_allclose(O.decode_attention(q[:1], k, v)[0], v[4], atol=1e-9)   # one key dominates
+    assert np.array_equal(O.decode_attention(q, k[:0], v[:0]), np.zeros((3, d)))
+
+
+def test_decode_attention_brute_force():
+    rng = np.random.default_rng(51)
+    q = rng.standard_normal((2, 4))
+    k = rng.standard_normal((5, 4))
+    v = rng.standard_normal((5, 3))
+    for i in range(2):
+        lg = [sum(q[i, t] * k[j, t] for t in range(4)) / 2.0 for j in range(5)]
+        z = math.fsum(math.exp(x) for x in lg)
+        want = [math.fsum(math.exp(lg[j]) / z * v[j, c] for j in range(5)) for c in range(3)]
+        np.testing.assert_allclose(O.decode_attention(q, k, v)[i], want, rtol=1e-13)
