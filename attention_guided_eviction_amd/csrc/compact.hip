@@ -2,13 +2,16 @@
 // k_out[r] = k[idx[r]], v_out[r] = v[idx[r]] for r < n_kept, as bit copies.
 //
 // Each thread moves one 16-byte chunk of a K row and the same chunk of the V row, so a
-// wavefront reads and writes whole 256-byte rows (head_dim 128) contiguously.
+// wavefront reads and writes whole 256-byte rows (head_dim 128) contiguously.  The outputs
+// are not read again by this event, so they are written with non-temporal stores (measured
+// on MI355X: 94 -> 74 us for the 7B shape's 470 MB moved, i.e. 6.4 TB/s).
 #include "bkv_internal.h"
 
 namespace bkv {
 namespace {
 
 constexpr int kThreads = 256;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void compact_kernel(const CompactArgs a, int blocks_per_unit) {
@@ -28,10 +31,10 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(const CompactArgs a, 
   src = src < 0 ? 0 : (src >= a.capacity ? a.capacity - 1 : src);
   const size_t in_off = (static_cast<size_t>(bh) * a.capacity + src) * D + part * 8;
   const size_t out_off = (static_cast<size_t>(bh) * a.out_capacity + r) * D + part * 8;
-  const uint4 kv = *reinterpret_cast<const uint4*>(a.k[layer] + in_off);
-  const uint4 vv = *reinterpret_cast<const uint4*>(a.v[layer] + in_off);
-  *reinterpret_cast<uint4*>(a.k_out[layer] + out_off) = kv;
-  *reinterpret_cast<uint4*>(a.v_out[layer] + out_off) = vv;
+  const u32x4 kv = *reinterpret_cast<const u32x4*>(a.k[layer] + in_off);
+  const u32x4 vv = *reinterpret_cast<const u32x4*>(a.v[layer] + in_off);
+  __builtin_nontemporal_store(kv, reinterpret_cast<u32x4*>(a.k_out[layer] + out_off));
+  __builtin_nontemporal_store(vv, reinterpret_cast<u32x4*>(a.v_out[layer] + out_off));
 }
 
 }  // namespace
