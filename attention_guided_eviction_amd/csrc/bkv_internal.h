@@ -107,7 +107,7 @@ hipError_t launch_score(const ScoreArgs& a, int n_layers, int head_dim, hipStrea
 // Statistics pass with the observation rows in registers, for units of at most kQsMaxRows
 // padded rows: resident workgroups per CU, and one launch on `grid` workgroups (a.n_layers,
 // a.slots and a.paired set by the caller; the finish pass runs on the same grid).
-constexpr int kQsMaxRows = 256;
+constexpr int kQsMaxRows = 384;
 hipError_t qs_stats_occupancy(int head_dim, int obs_pad, int* per_cu);
 hipError_t launch_qs_stats(const ScoreArgs& a, int head_dim, int grid, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, int n_layers, hipStream_t s);

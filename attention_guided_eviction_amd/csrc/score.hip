@@ -20,7 +20,7 @@
 // are simply read twice.  The segments of a unit are numbered by workgroup (the
 // workgroup holding a tile follows arithmetically from the split, see score_common.h),
 // so the finish pass finds every partial of a unit without any table.  For units of at
-// most 256 observation rows the stats pass is the register-resident one of score_qs.hip,
+// most 384 observation rows the stats pass is the register-resident one of score_qs.hip,
 // which writes the same partials.
 //
 // MFMA mapping (v_mfma_f32_32x32x16_bf16, four waves, each owning 64 keys of a tile).

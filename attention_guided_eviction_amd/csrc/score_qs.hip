@@ -2,10 +2,10 @@
 // and the sum of exp2 of its logits over a unit piece; BeaconKV page, Figure 5 (b), (c))
 // with the observation rows held in registers and the keys streamed through LDS.  Same
 // work split and statistics partials as the LDS-staged stats pass of score.hip, whose
-// finish pass consumes them; used when a unit has at most 8 blocks of 32 observation rows.
+// finish pass consumes them; used when a unit has at most 12 blocks of 32 observation rows.
 //
 // Per workgroup (4 waves) the observation row blocks are dealt round-robin to the waves:
-// wave w keeps blocks w and w + 4 in registers for the whole unit piece.  Every wave works
+// wave w keeps blocks w, w + 4 (and w + 8) in registers for the whole unit piece.  Every wave works
 // on every 32-key fragment, so a fragment is fetched from HBM once per workgroup, by all
 // four waves together, straight into LDS (`global_load_lds_dwordx4`, no registers), into
 // a ring of kSlots slots that keeps kSlots - 1 fragments in flight.  Each 16-byte key
@@ -311,8 +311,10 @@ __device__ void qs_stats_segment(const ScoreArgs& a, const UnitInfo& ui, int til
   RowStat st[BPW];
 #pragma unroll
   for (int b = 0; b < BPW; ++b) st[b] = RowStat{kNegInf, 0.f};
-  if (BPW == 2 && nb == 2) {
+  if (nb == BPW) {
     stats_loop<D, BPW, BPW>(kp, ui, key_begin, nf, ring, q, st, c);
+  } else if (BPW == 3 && nb == 2) {
+    stats_loop<D, BPW, (BPW > 2 ? 2 : 1)>(kp, ui, key_begin, nf, ring, q, st, c);
   } else if (nb == 1) {
     stats_loop<D, BPW, 1>(kp, ui, key_begin, nf, ring, q, st, c);
   } else {   // no rows: keep the workgroup's barrier count
@@ -347,8 +349,7 @@ constexpr size_t qs_lds_bytes() {
 }
 
 template <int D, int BPW>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void qs_stats_kernel(const ScoreArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t ring[];
+__device__ inline void qs_stats_body(const ScoreArgs& a, uint8_t* ring) {
   const int w = static_cast<int>(blockIdx.x);
   const int T = layer_tiles(a);
   Split sp;
@@ -377,12 +378,35 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
   }
 }
 
+// Up to two row blocks per wave fit in 256 registers (two waves per SIMD); three take one
+// wave per SIMD and its 512 registers.
+template <int D, int BPW>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void qs_stats_kernel(const ScoreArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t ring[];
+  qs_stats_body<D, BPW>(a, ring);
+}
+
+template <int D, int BPW>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void qs_stats_kernel_wide(
+    const ScoreArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t ring[];
+  qs_stats_body<D, BPW>(a, ring);
+}
+
+template <int D, int BPW>
+constexpr auto qs_kernel_of() {
+  if constexpr (BPW == 3)
+    return &qs_stats_kernel_wide<D, BPW>;
+  else
+    return &qs_stats_kernel<D, BPW>;
+}
+
 template <int D, int BPW>
 hipError_t prepare() {
   static std::once_flag once;
   static hipError_t err = hipSuccess;
   std::call_once(once, [] {
-    err = hipFuncSetAttribute(reinterpret_cast<const void*>(&qs_stats_kernel<D, BPW>),
+    err = hipFuncSetAttribute(reinterpret_cast<const void*>(qs_kernel_of<D, BPW>()),
                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(qs_lds_bytes<D>()));
   });
   return err;
@@ -392,28 +416,33 @@ template <int D, int BPW>
 hipError_t occupancy(int* per_cu) {
   hipError_t e = prepare<D, BPW>();
   if (e != hipSuccess) return note_hip_error(e, "score: hipFuncSetAttribute");
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, qs_stats_kernel<D, BPW>, kThreads, qs_lds_bytes<D>());
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, qs_kernel_of<D, BPW>(), kThreads, qs_lds_bytes<D>());
   return note_hip_error(e, "score: hipOccupancyMaxActiveBlocksPerMultiprocessor");
 }
 
 template <int D, int BPW>
 hipError_t launch(const ScoreArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((qs_stats_kernel<D, BPW>), dim3(grid), dim3(kThreads), qs_lds_bytes<D>(), s, a);
+  hipLaunchKernelGGL((qs_kernel_of<D, BPW>()), dim3(grid), dim3(kThreads), qs_lds_bytes<D>(), s, a);
   return note_hip_error(hipGetLastError(), "score: launch score_stats");
 }
 
 }  // namespace
 
+// Row blocks per wave: 1, 2 or 3 (up to 128, 256 or 384 padded rows).
+static int blocks_per_wave(int obs_pad) { return (obs_pad + kWaves * 32 - 1) / (kWaves * 32); }
+
 hipError_t qs_stats_occupancy(int head_dim, int obs_pad, int* per_cu) {
-  const bool two = obs_pad > kWaves * 32;
-  if (head_dim == 128) return two ? occupancy<128, 2>(per_cu) : occupancy<128, 1>(per_cu);
-  return two ? occupancy<64, 2>(per_cu) : occupancy<64, 1>(per_cu);
+  const int bpw = blocks_per_wave(obs_pad);
+  if (head_dim == 128) return bpw == 3 ? occupancy<128, 3>(per_cu) : bpw == 2 ? occupancy<128, 2>(per_cu)
+                                                                              : occupancy<128, 1>(per_cu);
+  return bpw == 3 ? occupancy<64, 3>(per_cu) : bpw == 2 ? occupancy<64, 2>(per_cu) : occupancy<64, 1>(per_cu);
 }
 
 hipError_t launch_qs_stats(const ScoreArgs& a, int head_dim, int grid, hipStream_t s) {
-  const bool two = a.obs_pad > kWaves * 32;
-  if (head_dim == 128) return two ? launch<128, 2>(a, grid, s) : launch<128, 1>(a, grid, s);
-  return two ? launch<64, 2>(a, grid, s) : launch<64, 1>(a, grid, s);
+  const int bpw = blocks_per_wave(a.obs_pad);
+  if (head_dim == 128)
+    return bpw == 3 ? launch<128, 3>(a, grid, s) : bpw == 2 ? launch<128, 2>(a, grid, s) : launch<128, 1>(a, grid, s);
+  return bpw == 3 ? launch<64, 3>(a, grid, s) : bpw == 2 ? launch<64, 2>(a, grid, s) : launch<64, 1>(a, grid, s);
 }
 
 }  // namespace bkv

@@ -55,6 +55,9 @@ EDGE = {
     # exactly 256 observation rows (7 * 32 + 32), the most the register-resident stats pass takes
     "obs_256": WORKLOADS["qwen7b_16k"].replace(n_layers=1, capacity=1300, seq_len=1291, budget=400, nb_init=32,
                                                nb_max=32),
+    # head_dim 64 with 11 row blocks (16 * 20 + 32 = 352 rows): three blocks on some waves
+    "three_blocks_d64": WORKLOADS["tiny"].replace(n_q_heads=32, n_kv_heads=2, window=20, nb_init=32, nb_max=32,
+                                                  t_new=0, capacity=1200, seq_len=1177, budget=300),
     # window equals budget: nothing chosen by score
     "window_eq_budget": WORKLOADS["tiny"].replace(window=8, budget=8, t_new=0, capacity=400, seq_len=400),
     # more layers than one launch holds (48)
