@@ -5,8 +5,9 @@
 // the unit's scores in registers as bit patterns (non-negative fp32 order like unsigned
 // integers).  The k-th largest pattern T among the positions before the window is found
 // by a most-significant-digit-first radix select: four passes over 8-bit digits, each an
-// LDS histogram of the candidates that still match the digits chosen so far, scanned by
-// one wave.  Every score above T is kept and, of the scores equal to T, the lowest
+// LDS histogram of the candidates that still match the digits chosen so far (built in 16
+// lane-indexed copies and then folded, since the leading digits of probabilities pile up
+// on a few bins), scanned by one wave.  Every score above T is kept and, of the scores equal to T, the lowest
 // positions fill the remaining slots; one block-wide scan of (ties, kept) counts in
 // position order gives every thread its tie rank and its output offset, so the kept
 // positions come out in ascending order.
@@ -16,6 +17,11 @@ namespace bkv {
 namespace {
 
 constexpr int kWaves = kSelectThreads / 64;
+// Histogram copies indexed by lane: lanes of one wave whose digits agree (common for the
+// leading digit of probabilities) add to different copies instead of queueing on one LDS
+// address; the odd stride puts the copies of a bin in different banks.
+constexpr int kCopies = 16;
+constexpr int kCopyStride = 257;
 
 // Exclusive prefix over the block (thread order) of a 64-bit value.  `buf` holds kWaves
 // entries; one barrier.
@@ -74,6 +80,7 @@ __device__ inline void pick_digit(int* hist, int r, int* out) {
 template <int EPT>
 __global__ __launch_bounds__(kSelectThreads) void select_topk_kernel(const SelectArgs a) {
   __shared__ __attribute__((aligned(16))) int hist[256];
+  __shared__ int histc[kCopies * kCopyStride];
   __shared__ unsigned long long scan_buf[kWaves];
   __shared__ int pick[2];
   const int u = blockIdx.x;
@@ -118,7 +125,9 @@ __global__ __launch_bounds__(kSelectThreads) void select_topk_kernel(const Selec
   int need_eq = 0;   // ties at T to keep, lowest positions first
   if (want > 0) {
     if (tid < 64) *reinterpret_cast<int4*>(hist + 4 * tid) = make_int4(0, 0, 0, 0);
+    for (int i = tid; i < kCopies * kCopyStride; i += kSelectThreads) histc[i] = 0;
     __syncthreads();
+    int* my_copy = histc + (tid & (kCopies - 1)) * kCopyStride;
     uint32_t P = 0;
     int r = want;
 #pragma unroll
@@ -127,7 +136,17 @@ __global__ __launch_bounds__(kSelectThreads) void select_topk_kernel(const Selec
 #pragma unroll
       for (int i = 0; i < EPT; ++i) {
         const bool match = j0 + i < prefix && (pass == 0 || (x[i] >> (shift + 8)) == P);
-        if (match) atomicAdd(&hist[(x[i] >> shift) & 255u], 1);
+        if (match) atomicAdd(&my_copy[(x[i] >> shift) & 255u], 1);
+      }
+      __syncthreads();
+      if (tid < 256) {   // fold the copies (and clear them for the next pass)
+        int sum = 0;
+#pragma unroll
+        for (int c = 0; c < kCopies; ++c) {
+          sum += histc[c * kCopyStride + tid];
+          histc[c * kCopyStride + tid] = 0;
+        }
+        hist[tid] = sum;
       }
       __syncthreads();
       if (tid < 64) pick_digit(hist, r, pick);
