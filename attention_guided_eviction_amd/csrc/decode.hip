@@ -25,6 +25,7 @@ typedef const __attribute__((address_space(4))) uint32_t* const_u32;
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr float kNegInf = -__builtin_inff();
+constexpr int kValueUnroll = 4;   // value-row loads in flight per wave
 
 __device__ inline float dot2(uint32_t x, uint32_t y, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), __builtin_bit_cast(bf16x2, y), acc, false);
@@ -45,14 +46,14 @@ __device__ inline float wave_sum(float v) {
 __device__ inline float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ inline float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
 
-template <int D>
+template <int D, int G>
 __global__ __launch_bounds__(kThreads) void decode_partial(const DecodeArgs a) {
   constexpr int W = D / 2;                 // 32-bit words per row
   constexpr int kLanesPerRow = D / 8;      // 16-byte pieces per row in the value loads
   constexpr int kRowsPerLoad = 64 / kLanesPerRow;
-  __shared__ float pbuf[kWaves][kDecodeMaxGroup][64];
-  __shared__ float m_w[kWaves][kDecodeMaxGroup], z_w[kWaves][kDecodeMaxGroup];
-  __shared__ float o_w[kWaves][kDecodeMaxGroup][D];
+  __shared__ float pbuf[kWaves][G][64];
+  __shared__ float m_w[kWaves][G], z_w[kWaves][G];
+  __shared__ float o_w[kWaves][G][D];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -67,14 +68,13 @@ __global__ __launch_bounds__(kThreads) void decode_partial(const DecodeArgs a) {
   L = L < 0 ? 0 : (L > a.capacity ? a.capacity : L);
   const int key_begin = chunk * kDecodeChunk;
   if (key_begin >= L) return;   // the merge reads only the chunks below L
-  const int G = a.group;
   const uint16_t* kp = a.k[layer] + static_cast<size_t>(bh) * a.capacity * D;
   const uint16_t* vp = a.v[layer] + static_cast<size_t>(bh) * a.capacity * D;
   const uint16_t* qp = a.q[layer] + (static_cast<size_t>(b) * a.n_q_heads + h * G) * D;
 
-  float m[kDecodeMaxGroup], z[kDecodeMaxGroup], o[kDecodeMaxGroup][8];
+  float m[G], z[G], o[G][8];
 #pragma unroll
-  for (int g = 0; g < kDecodeMaxGroup; ++g) {
+  for (int g = 0; g < G; ++g) {
     m[g] = kNegInf;
     z[g] = 0.f;
 #pragma unroll
@@ -98,40 +98,35 @@ __global__ __launch_bounds__(kThreads) void decode_partial(const DecodeArgs a) {
       kr[4 * i + 2] = x.z;
       kr[4 * i + 3] = x.w;
     }
-    float t[kDecodeMaxGroup];
+    float t[G];
 #pragma unroll
-    for (int g = 0; g < kDecodeMaxGroup; ++g) {
-      t[g] = kNegInf;
-      if (g < G) {
-        const const_u32 qg = (const_u32)(qp + static_cast<size_t>(g) * D);   // uniform: scalar loads
-        float acc0 = 0.f, acc1 = 0.f;
+    for (int g = 0; g < G; ++g) {
+      const const_u32 qg = (const_u32)(qp + static_cast<size_t>(g) * D);   // uniform: scalar loads
+      float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
-        for (int i = 0; i < W; i += 2) {
-          acc0 = dot2(kr[i], qg[i], acc0);
-          acc1 = dot2(kr[i + 1], qg[i + 1], acc1);
-        }
-        t[g] = k0 + lane < L ? (acc0 + acc1) * a.scale_log2 : kNegInf;
+      for (int i = 0; i < W; i += 2) {
+        acc0 = dot2(kr[i], qg[i], acc0);
+        acc1 = dot2(kr[i + 1], qg[i + 1], acc1);
       }
+      t[g] = k0 + lane < L ? (acc0 + acc1) * a.scale_log2 : kNegInf;
     }
     // running softmax per query; weights of this block to LDS
 #pragma unroll
-    for (int g = 0; g < kDecodeMaxGroup; ++g) {
-      if (g < G) {
-        const float mb = wave_max(t[g]);
-        const float mn = fmaxf(m[g], mb);
-        const float scale = m[g] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m[g] - mn);
-        const float p = __builtin_amdgcn_exp2f(t[g] - mn);
-        z[g] = z[g] * scale + wave_sum(p);
+    for (int g = 0; g < G; ++g) {
+      const float mb = wave_max(t[g]);
+      const float mn = fmaxf(m[g], mb);
+      const float scale = m[g] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m[g] - mn);
+      const float p = __builtin_amdgcn_exp2f(t[g] - mn);
+      z[g] = z[g] * scale + wave_sum(p);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[g][e] *= scale;
-        m[g] = mn;
-        pbuf[wave][g][lane] = p;
-      }
+      for (int e = 0; e < 8; ++e) o[g][e] *= scale;
+      m[g] = mn;
+      pbuf[wave][g][lane] = p;
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     // weighted value rows: lanes read whole rows, rows vrow, vrow + kRowsPerLoad, ...
-#pragma unroll 4
+#pragma unroll kValueUnroll
     for (int r0 = 0; r0 < 64; r0 += kRowsPerLoad) {
       const int j = r0 + vrow;
       int vk = k0 + j;
@@ -140,12 +135,10 @@ __global__ __launch_bounds__(kThreads) void decode_partial(const DecodeArgs a) {
       const float v8[8] = {bf16_lo(x.x), bf16_hi(x.x), bf16_lo(x.y), bf16_hi(x.y),
                            bf16_lo(x.z), bf16_hi(x.z), bf16_lo(x.w), bf16_hi(x.w)};
 #pragma unroll
-      for (int g = 0; g < kDecodeMaxGroup; ++g) {
-        if (g < G) {
-          const float p = pbuf[wave][g][j];
+      for (int g = 0; g < G; ++g) {
+        const float p = pbuf[wave][g][j];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) o[g][e] = fmaf(p, v8[e], o[g][e]);
-        }
+        for (int e = 0; e < 8; ++e) o[g][e] = fmaf(p, v8[e], o[g][e]);
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -153,23 +146,21 @@ __global__ __launch_bounds__(kThreads) void decode_partial(const DecodeArgs a) {
   }
   // the lanes holding the same dims (lane % kLanesPerRow) add their rows' contributions
 #pragma unroll
-  for (int g = 0; g < kDecodeMaxGroup; ++g) {
-    if (g < G) {
+  for (int g = 0; g < G; ++g) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float s = o[g][e];
+    for (int e = 0; e < 8; ++e) {
+      float s = o[g][e];
 #pragma unroll
-        for (int off = kLanesPerRow; off < 64; off <<= 1) s += __shfl_xor(s, off);
-        o[g][e] = s;
-      }
-      if (lane < kLanesPerRow) {
+      for (int off = kLanesPerRow; off < 64; off <<= 1) s += __shfl_xor(s, off);
+      o[g][e] = s;
+    }
+    if (lane < kLanesPerRow) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o_w[wave][g][vcol + e] = o[g][e];
-      }
-      if (lane == 0) {
-        m_w[wave][g] = m[g];
-        z_w[wave][g] = z[g];
-      }
+      for (int e = 0; e < 8; ++e) o_w[wave][g][vcol + e] = o[g][e];
+    }
+    if (lane == 0) {
+      m_w[wave][g] = m[g];
+      z_w[wave][g] = z[g];
     }
   }
   __syncthreads();
@@ -226,23 +217,39 @@ __global__ __launch_bounds__(D) void decode_merge(const DecodeArgs a) {
   a.out[layer][(static_cast<size_t>(b) * a.n_q_heads + hq) * D + d] = Z > 0.f ? O / Z : 0.f;
 }
 
+template <int D, int G>
+hipError_t launch_d(const DecodeArgs& a, unsigned grid1, unsigned grid2, hipStream_t s) {
+  hipLaunchKernelGGL((decode_partial<D, G>), dim3(grid1), dim3(kThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return note_hip_error(e, "decode: launch partial");
+  hipLaunchKernelGGL(decode_merge<D>, dim3(grid2), dim3(D), 0, s, a);
+  return note_hip_error(hipGetLastError(), "decode: launch merge");
+}
+
+template <int D>
+hipError_t launch_g(const DecodeArgs& a, unsigned grid1, unsigned grid2, hipStream_t s) {
+  static_assert(kDecodeMaxGroup == 8, "one instantiation per group size");
+  switch (a.group) {
+    case 1: return launch_d<D, 1>(a, grid1, grid2, s);
+    case 2: return launch_d<D, 2>(a, grid1, grid2, s);
+    case 3: return launch_d<D, 3>(a, grid1, grid2, s);
+    case 4: return launch_d<D, 4>(a, grid1, grid2, s);
+    case 5: return launch_d<D, 5>(a, grid1, grid2, s);
+    case 6: return launch_d<D, 6>(a, grid1, grid2, s);
+    case 7: return launch_d<D, 7>(a, grid1, grid2, s);
+    case 8: return launch_d<D, 8>(a, grid1, grid2, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
 
+// One partial kernel per (head_dim, group size): the per-query registers (running max, sum
+// and eight output dims) and LDS scale with the group, so small groups run more waves.
 hipError_t launch_decode(const DecodeArgs& a, int n_layers, int head_dim, hipStream_t s) {
   const unsigned grid1 = static_cast<unsigned>(n_layers) * a.batch * a.n_kv_heads * a.chunks;
   const unsigned grid2 = static_cast<unsigned>(n_layers) * a.batch * a.n_q_heads;
-  if (head_dim == 128) {
-    hipLaunchKernelGGL(decode_partial<128>, dim3(grid1), dim3(kThreads), 0, s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return note_hip_error(e, "decode: launch partial");
-    hipLaunchKernelGGL(decode_merge<128>, dim3(grid2), dim3(128), 0, s, a);
-  } else {
-    hipLaunchKernelGGL(decode_partial<64>, dim3(grid1), dim3(kThreads), 0, s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return note_hip_error(e, "decode: launch partial");
-    hipLaunchKernelGGL(decode_merge<64>, dim3(grid2), dim3(64), 0, s, a);
-  }
-  return note_hip_error(hipGetLastError(), "decode: launch merge");
+  return head_dim == 128 ? launch_g<128>(a, grid1, grid2, s) : launch_g<64>(a, grid1, grid2, s);
 }
 
 }  // namespace bkv

@@ -71,3 +71,19 @@ def test_decode_over_compacted_cache():
     bkv.decode_attention(shape, q, ev.k_out, ev.v_out, out, ws)
     torch.cuda.synchronize()
     log(f"[decode] compacted: worst abs error {_check(shape, q, ev.k_out, ev.v_out, out):.2e}")
+
+
+@pytest.mark.parametrize("G", range(1, 9))
+@pytest.mark.parametrize("D", [64, 128])
+def test_decode_every_group_size(G, D):
+    """One partial kernel per (head_dim, group size): each is checked, with a ragged tail
+    inside the second 1024-key chunk and a sequence shorter than one 64-key block."""
+    gen = torch.Generator(device="cuda").manual_seed(100 * G + D)
+    seq = torch.tensor((1100, 37), dtype=torch.int32, device="cuda")
+    shape = bkv.CacheShape(1, 2, 2 * G, 2, D, 1100, seq)
+    q, k, v = _random(shape, gen, 1.5)
+    out = [torch.empty((2, 2 * G, D), dtype=torch.float32, device="cuda")]
+    ws = bkv.alloc_workspace(bkv.decode_workspace_bytes(shape))
+    bkv.decode_attention(shape, q, k, v, out, ws)
+    torch.cuda.synchronize()
+    log(f"[decode] G {G} D {D}: worst abs error {_check(shape, q, k, v, out):.2e}")
