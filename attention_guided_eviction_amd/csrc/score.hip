@@ -368,42 +368,57 @@ __device__ inline f32x16 load_seed(const float* nlse, int qb) {
   return o;
 }
 
-// Folds the block in `cur` into vm[f] (fragment f) while the products of the next block
-// (accumulators seeded with `seed`) go into `nxt`; then the rows of block nq are loaded
-// into qf and the seed of block nq into seed_next.  MEAN: vm sums the attention weights
+// Products of block k (rows in qk, accumulators X already seeded with -lse2 / c) while the
+// accumulators P of the previous block are folded into vm (FOLD); the rows of block kn go
+// to qn at the start of the step and, once P is folded, the seed of block kn to P, so both
+// loads are in flight behind this step's products.  MEAN: vm sums the attention weights
 // exp2(c * acc); otherwise vm is the running max of acc.
+//
+// The max is IEEE-2019 maximum (v_maximum3_f32, NaN-propagating), not fmaxf: the operands
+// come straight from the matrix unit, and fmaxf's number-preferring semantics make the
+// compiler quiet each of them with an extra v_max_f32 first (3.5 vector instructions per
+// two logits instead of one).  Logits of finite inputs are never NaN.
 template <bool MEAN>
 __device__ inline void fold2(float& vm, float x0, float x1, float c) {
   if (MEAN)
     vm += __builtin_amdgcn_exp2f(c * x0) + __builtin_amdgcn_exp2f(c * x1);
   else
-    vm = fmaxf(vm, fmaxf(x0, x1));
+    vm = __builtin_elementwise_maximum(__builtin_elementwise_maximum(vm, x0), x1);
 }
 
-template <int D, bool MEAN>
-__device__ inline void finish_step(const KeyFrag<D>& kf, bf16x8 (&qf)[D / 16], const f32x16 (&cur)[2],
-                                   f32x16 (&nxt)[2], const f32x16& seed, f32x16& seed_next, const uint8_t* qs,
-                                   const float* nlse, int nq, float c, float (&vm)[2]) {
-  f32x16 n0 = seed, n1 = seed;
-  constexpr int kPer = 16 / (D / 16);   // (row, key) pairs of each fragment per MFMA step
+template <int D, bool MEAN, bool FOLD>
+__device__ inline void finish_step(const KeyFrag<D>& kf, const bf16x8 (&qk)[D / 16], bf16x8 (&qn)[D / 16],
+                                   f32x16 (&X)[2], f32x16 (&P)[2], const uint8_t* qs, const float* nlse, int kn,
+                                   float c, float (&vm)[2]) {
+  constexpr int S = D / 16;
+  constexpr int kHalf = S / 2;
+  constexpr int kPer = 32 / kHalf;   // (row, key) pairs of each fragment folded per early k-step
+  load_qfrag<D>(qs, kn, qn);
+  f32x16 n0 = X[0], n1 = X[1];
 #pragma unroll
-  for (int st = 0; st < D / 16; ++st) {
-    n0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[st], kf.v[0][st], n0, 0, 0, 0);
-    n1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[st], kf.v[1][st], n1, 0, 0, 0);
+  for (int st = 0; st < S; ++st) {
+    n0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qk[st], kf.v[0][st], n0, 0, 0, 0);
+    n1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qk[st], kf.v[1][st], n1, 0, 0, 0);
+    if (FOLD && st < kHalf) {
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
+      for (int f = 0; f < 2; ++f)
 #pragma unroll
-      for (int j = 0; j < kPer; j += 2) fold2<MEAN>(vm[f], cur[f][st * kPer + j], cur[f][st * kPer + j + 1], c);
+        for (int j = 0; j < kPer / 2; j += 2) fold2<MEAN>(vm[f], P[f][st * kPer / 2 + j], P[f][st * kPer / 2 + j + 1], c);
+    }
   }
+  const f32x16 sd = load_seed(nlse, kn);
+  P[0] = sd;
+  P[1] = sd;
+  __builtin_amdgcn_sched_group_barrier(0x100, S, 0);                           // DS read: rows
 #pragma unroll
-  for (int st = 0; st < D / 16; ++st) {
+  for (int st = 0; st < kHalf; ++st) {
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                          // MFMA
-    __builtin_amdgcn_sched_group_barrier(MEAN ? 0x402 : 0x002, MEAN ? 3 * kPer : kPer, 0);   // VALU
+    if (FOLD) __builtin_amdgcn_sched_group_barrier(MEAN ? 0x402 : 0x002, MEAN ? 3 * kPer / 2 : kPer / 2, 0);   // fold
   }
-  seed_next = load_seed(nlse, nq);
-  load_qfrag<D>(qs, nq, qf);
-  nxt[0] = n0;
-  nxt[1] = n1;
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);                           // DS read: seed
+  __builtin_amdgcn_sched_group_barrier(0x008, 2 * (S - kHalf), 0);             // MFMA
+  X[0] = n0;
+  X[1] = n1;
 }
 
 template <bool MEAN>
@@ -416,35 +431,26 @@ __device__ inline void finish_last(const f32x16 (&cur)[2], float c, float (&vm)[
 
 // One wave's 64 keys: returns, in lane l, for key l of the wave (fragment l >> 5, key
 // l & 31) the max over all rows of x - lse2 / c, or with MEAN the sum over all rows of the
-// attention weights.
+// attention weights.  Blocks alternate between two row and two accumulator register sets.
 template <int D, bool MEAN>
 __device__ inline float finish_tile(const KeyFrag<D>& kf, const uint8_t* qs, const float* nlse, int nqb, float c) {
   const int lane = threadIdx.x & 63;
   float vm[2] = {MEAN ? 0.f : kNegInf, MEAN ? 0.f : kNegInf};
-  bf16x8 qf[D / 16];
+  bf16x8 q0[D / 16], q1[D / 16];
   f32x16 A[2], B[2];
-  f32x16 sa = load_seed(nlse, 0);
-  load_qfrag<D>(qs, 0, qf);
-  {
-    f32x16 c0 = sa, c1 = sa;
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[s], kf.v[0][s], c0, 0, 0, 0);
-      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[s], kf.v[1][s], c1, 0, 0, 0);
-    }
-    A[0] = c0;
-    A[1] = c1;
+  load_qfrag<D>(qs, 0, q0);
+  A[0] = load_seed(nlse, 0);
+  A[1] = A[0];
+  const int last = nqb - 1;
+  auto nxt = [&](int k) { return k < last ? k : last; };
+  finish_step<D, MEAN, false>(kf, q0, q1, A, B, qs, nlse, nxt(1), c, vm);
+  int k = 1;
+  for (; k + 1 < nqb; k += 2) {
+    finish_step<D, MEAN, true>(kf, q1, q0, B, A, qs, nlse, nxt(k + 1), c, vm);
+    finish_step<D, MEAN, true>(kf, q0, q1, A, B, qs, nlse, nxt(k + 2), c, vm);
   }
-  const int b1 = nqb > 1 ? 1 : 0;
-  f32x16 sb = load_seed(nlse, b1);
-  load_qfrag<D>(qs, b1, qf);
-  int qb = 0;
-  for (; qb + 2 < nqb; qb += 2) {
-    finish_step<D, MEAN>(kf, qf, A, B, sb, sa, qs, nlse, qb + 2, c, vm);
-    finish_step<D, MEAN>(kf, qf, B, A, sa, sb, qs, nlse, qb + 3 < nqb ? qb + 3 : nqb - 1, c, vm);
-  }
-  if (qb + 1 < nqb) {
-    finish_step<D, MEAN>(kf, qf, A, B, sb, sa, qs, nlse, qb + 1, c, vm);
+  if (k < nqb) {
+    finish_step<D, MEAN, true>(kf, q1, q0, B, A, qs, nlse, nxt(k + 1), c, vm);
     finish_last<MEAN>(B, c, vm);
   } else {
     finish_last<MEAN>(A, c, vm);

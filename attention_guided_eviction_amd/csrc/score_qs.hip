@@ -171,8 +171,10 @@ __device__ inline void stat_exact(const f32x16& acc, float c, RowStat& st) {
 // Cheap update against the running max of earlier fragments; falls back to the exact
 // update when a term may have overflowed (a logit ~64 above the running max, or the
 // row's first fragment while the max is still -inf).
+constexpr float kFastSumLimit = 1.8e19f;
+
 __device__ inline void stat_commit(const f32x16& acc, float zt, float c, RowStat& st) {
-  if (zt <= 1.8e19f)
+  if (zt <= kFastSumLimit)
     st.z += zt;
   else
     stat_exact(acc, c, st);
@@ -215,11 +217,25 @@ __device__ inline void stats_step(const KeyRegs<D>& k, const RowRegs<D, BPW>& q,
     __builtin_amdgcn_sched_group_barrier(0x402, 3 * kPer * NB, 0);   // VALU / transcendental
     __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);              // MFMA
   }
+  // One branch for all blocks: every block's sum feeds its condition, so the exp2 work of
+  // every block stays in the basic block of the products instead of sinking past an
+  // earlier block's overflow branch.
+  float zt[NB];
+  bool fast = true;
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    stat_commit(x[b], zs[b][0] + zs[b][1], c, st[b]);
-    nxt[b] = n[b];
+    zt[b] = zs[b][0] + zs[b][1];
+    fast = fast && zt[b] <= kFastSumLimit;
   }
+  if (fast) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) st[b].z += zt[b];
+  } else {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) stat_commit(x[b], zt[b], c, st[b]);
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b) nxt[b] = n[b];
 }
 
 template <int D, int BPW, int NB>
