@@ -147,15 +147,16 @@ bkv_status hip_status(hipError_t e) { return e == hipSuccess ? BKV_OK : BKV_EHIP
 
 struct DecodeWs {
   size_t m_bytes, o_bytes, total;
-  int chunks;
+  int chunk_keys, chunks;
 };
 
 // Partials of the largest launch (kMaxLayers layers or all of them).
 DecodeWs decode_ws(const bkv_shape* s) {
   DecodeWs w{};
-  w.chunks = (s->capacity + kDecodeChunk - 1) / kDecodeChunk;
-  const size_t cells = static_cast<size_t>(std::min(s->n_layers, kMaxLayers)) * s->batch * s->n_kv_heads *
-                       kDecodeMaxGroup * w.chunks;
+  const long long launch_units = static_cast<long long>(std::min(s->n_layers, kMaxLayers)) * s->batch * s->n_kv_heads;
+  w.chunk_keys = decode_chunk_keys(launch_units, s->capacity);
+  w.chunks = (s->capacity + w.chunk_keys - 1) / w.chunk_keys;
+  const size_t cells = static_cast<size_t>(launch_units) * kDecodeMaxGroup * w.chunks;
   w.m_bytes = align_up(cells * sizeof(float));
   w.o_bytes = align_up(cells * static_cast<size_t>(s->head_dim) * sizeof(float));
   w.total = 2 * w.m_bytes + w.o_bytes;
@@ -432,6 +433,7 @@ bkv_status bkv_decode_attention(const bkv_shape* shape, const void* const* q, co
   a.n_kv_heads = shape->n_kv_heads;
   a.group = g;
   a.capacity = shape->capacity;
+  a.chunk_keys = ws.chunk_keys;
   a.chunks = ws.chunks;
   a.scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(shape->head_dim)));
   for (int l0 = 0; l0 < shape->n_layers; l0 += kMaxLayers) {

@@ -39,12 +39,22 @@ struct ScoreArgs {
   float scale_log2;     // log2(e) / sqrt(head_dim)
 };
 
+// Share weights of the older : newer workgroup of each CU when two run on it (workgroups w
+// and w + grid/2): the wave arbiter favours the older one, so equal shares leave the newer
+// one finishing last.  Measured on MI355X per pass from per-workgroup timestamps.  The
+// stats weights also number the statistics partials, so both passes and both stats
+// implementations use them.
+constexpr int kStatsWeightOld = 9, kStatsWeightNew = 7;
+constexpr int kFinishWeightOld = 15, kFinishWeightNew = 13;
+
 // Statistics slots per unit for a launch of n_layers layers (the workspace is sized from
-// this): one per workgroup that can share a unit (the smallest share is at least 4/5 of
-// the mean), never more than the unit's tiles.
+// this): one per workgroup that can share a unit, never more than the unit's tiles.  The
+// smallest stats share is 2 B / (A + B) of the mean (weights A : B), so at most
+// grid (A + B) / (2 B) / units + 2 workgroups meet one unit.
 inline int score_slots(int capacity, int n_layers, int n_kv_heads) {
   const int tiles = (capacity + kScoreTile - 1) / kScoreTile;
-  const int sharing = kScoreMaxGrid * 5 / 4 / (n_layers * n_kv_heads) + 2;   // share weights up to 3:2
+  const int sharing = kScoreMaxGrid * (kStatsWeightOld + kStatsWeightNew) / (2 * kStatsWeightNew) /
+                          (n_layers * n_kv_heads) + 2;
   return tiles < sharing ? tiles : sharing;
 }
 
@@ -85,8 +95,22 @@ struct FpsArgs {
 
 // ---- decode attention ----------------------------------------------------------------------
 
-constexpr int kDecodeChunk = 1024;     // keys per workgroup (4 waves x 256)
 constexpr int kDecodeMaxGroup = 8;     // query heads per KV head
+
+// Keys per decode workgroup (4 waves, each a quarter in blocks of 64 keys): 1024, or 512 or
+// 256 when larger chunks would leave fewer than kDecodeMinGrid workgroups per launch (about
+// 1.25 per CU of MI355X).  Measured: a 64-unit launch over 2048 keys took 34 us with 1024-key
+// chunks and 25 us with 256; a 112-unit launch over 4096 keys (448 workgroups) was 4% faster
+// with 1024 than with 256.
+constexpr int kDecodeMaxChunk = 1024;
+constexpr int kDecodeMinChunk = 256;
+constexpr int kDecodeMinGrid = 320;
+inline int decode_chunk_keys(long long launch_units, int capacity) {
+  int c = kDecodeMaxChunk;
+  while (c > kDecodeMinChunk && launch_units * ((capacity + c - 1) / c) < kDecodeMinGrid)
+    c /= 2;
+  return c;
+}
 
 struct DecodeArgs {
   const uint16_t* q[kMaxLayers];     // [batch][n_q_heads][head_dim]
@@ -98,7 +122,8 @@ struct DecodeArgs {
   float* part_z;                     // same cells: sum of exp2(t - m)
   float* part_o;                     // [cell][head_dim] unnormalised output
   int batch, n_q_heads, n_kv_heads, group, capacity;
-  int chunks;                        // ceil(capacity / kDecodeChunk)
+  int chunk_keys;                    // keys per workgroup (decode_chunk_keys)
+  int chunks;                        // ceil(capacity / chunk_keys)
   float scale_log2;
 };
 

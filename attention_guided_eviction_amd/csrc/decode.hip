@@ -5,8 +5,10 @@
 //
 // Memory-bound (each K and V row is read once per step for the G query heads sharing
 // it), so the kernel is built around the loads rather than the matrix units:
-//   decode_partial  one workgroup per (layer, sequence, KV head, 1024-key chunk); each
-//                   wave takes 256 keys in four blocks of 64.  Logits: lane = key, the key
+//   decode_partial  one workgroup per (layer, sequence, KV head, chunk of 1024 keys, or 512
+//                   or 256 where 1024 would leave the launch too few workgroups to fill the
+//                   chip); each wave takes a quarter of the chunk in blocks of 64 keys.
+//                   Logits: lane = key, the key
 //                   row in registers, the G query rows read through scalar loads as SGPR
 //                   operands of v_dot2_f32_bf16.  Values: lanes 16 k + j read row k's dims
 //                   8 j .. 8 j + 7, so every load instruction reads whole 256-byte rows; the
@@ -46,7 +48,7 @@ __device__ inline float wave_sum(float v) {
 __device__ inline float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ inline float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
 
-template <int D, int G>
+template <int D, int G, int NB>
 __global__ __launch_bounds__(kThreads) void decode_partial(const DecodeArgs a) {
   constexpr int W = D / 2;                 // 32-bit words per row
   constexpr int kLanesPerRow = D / 8;      // 16-byte pieces per row in the value loads
@@ -66,7 +68,7 @@ __global__ __launch_bounds__(kThreads) void decode_partial(const DecodeArgs a) {
   const int h = bh - b * a.n_kv_heads;
   int L = a.seq_len[b];
   L = L < 0 ? 0 : (L > a.capacity ? a.capacity : L);
-  const int key_begin = chunk * kDecodeChunk;
+  const int key_begin = chunk * (kWaves * 64 * NB);
   if (key_begin >= L) return;   // the merge reads only the chunks below L
   const uint16_t* kp = a.k[layer] + static_cast<size_t>(bh) * a.capacity * D;
   const uint16_t* vp = a.v[layer] + static_cast<size_t>(bh) * a.capacity * D;
@@ -83,8 +85,8 @@ __global__ __launch_bounds__(kThreads) void decode_partial(const DecodeArgs a) {
   const int vrow = lane / kLanesPerRow;    // row of the value load within a group of rows
   const int vcol = (lane % kLanesPerRow) * 8;
 
-  for (int blk = 0; blk < 4; ++blk) {
-    const int k0 = key_begin + wave * 256 + blk * 64;
+  for (int blk = 0; blk < NB; ++blk) {
+    const int k0 = key_begin + (wave * NB + blk) * 64;
     if (k0 >= L) break;   // uniform across the wave
     // logits of key k0 + lane for every query of the group
     const int key = k0 + lane < L ? k0 + lane : L - 1;
@@ -201,7 +203,7 @@ __global__ __launch_bounds__(D) void decode_merge(const DecodeArgs a) {
   const int g = hq - h * a.group;
   int L = a.seq_len[b];
   L = L < 0 ? 0 : (L > a.capacity ? a.capacity : L);
-  const int n = (L + kDecodeChunk - 1) / kDecodeChunk;
+  const int n = (L + a.chunk_keys - 1) / a.chunk_keys;
   const int u = (layer * a.batch + b) * a.n_kv_heads + h;
   const size_t base = (static_cast<size_t>(u) * kDecodeMaxGroup + g) * a.chunks;
   const int d = threadIdx.x;
@@ -219,7 +221,15 @@ __global__ __launch_bounds__(D) void decode_merge(const DecodeArgs a) {
 
 template <int D, int G>
 hipError_t launch_d(const DecodeArgs& a, unsigned grid1, unsigned grid2, hipStream_t s) {
-  hipLaunchKernelGGL((decode_partial<D, G>), dim3(grid1), dim3(kThreads), 0, s, a);
+  static_assert(kDecodeMaxChunk == kWaves * 64 * 4 && kDecodeMinChunk == kWaves * 64, "1, 2 or 4 blocks per wave");
+  if (a.chunk_keys == kDecodeMaxChunk)
+    hipLaunchKernelGGL((decode_partial<D, G, 4>), dim3(grid1), dim3(kThreads), 0, s, a);
+  else if (a.chunk_keys == kDecodeMaxChunk / 2)
+    hipLaunchKernelGGL((decode_partial<D, G, 2>), dim3(grid1), dim3(kThreads), 0, s, a);
+  else if (a.chunk_keys == kDecodeMinChunk)
+    hipLaunchKernelGGL((decode_partial<D, G, 1>), dim3(grid1), dim3(kThreads), 0, s, a);
+  else
+    return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return note_hip_error(e, "decode: launch partial");
   hipLaunchKernelGGL(decode_merge<D>, dim3(grid2), dim3(D), 0, s, a);

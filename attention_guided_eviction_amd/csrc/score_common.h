@@ -122,12 +122,6 @@ struct Split {
 };
 
 
-// Share weights of the older : newer workgroup of each CU, measured on MI355X (with equal
-// shares the older workgroups finished the stats pass in 126 us against 153 us, the
-// finish pass in 103 us against 117 us).  The stats weights also number the statistics
-// partials, so both passes and both stats implementations use these.
-constexpr int kStatsWeightOld = 9, kStatsWeightNew = 7;
-constexpr int kFinishWeightOld = 15, kFinishWeightNew = 13;
 
 // ---- per-unit data ------------------------------------------------------------------------
 

@@ -87,3 +87,21 @@ def test_decode_every_group_size(G, D):
     bkv.decode_attention(shape, q, k, v, out, ws)
     torch.cuda.synchronize()
     log(f"[decode] G {G} D {D}: worst abs error {_check(shape, q, k, v, out):.2e}")
+
+
+@pytest.mark.parametrize("n_layers,B,Hkv,cap,lens", [
+    (4, 10, 8, 1100, (1100, 1025, 3, 0, 700, 1024, 1099, 64, 65, 512)),   # 640 workgroups of 1024 keys
+    (3, 5, 8, 1500, (1500, 1, 1025, 513, 257)),                           # 120 units: 512-key chunks
+])
+def test_decode_chunk_sizes(n_layers, B, Hkv, cap, lens):
+    """The chunk size follows the launch size (1024 keys per workgroup for large launches,
+    512 or 256 for small ones); these shapes take the 1024- and 512-key kernels."""
+    gen = torch.Generator(device="cuda").manual_seed(n_layers * 100 + B)
+    seq = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    shape = bkv.CacheShape(n_layers, B, 2 * Hkv, Hkv, 64, cap, seq)
+    q, k, v = _random(shape, gen, 1.5)
+    out = [torch.empty((B, 2 * Hkv, 64), dtype=torch.float32, device="cuda") for _ in range(n_layers)]
+    ws = bkv.alloc_workspace(bkv.decode_workspace_bytes(shape))
+    bkv.decode_attention(shape, q, k, v, out, ws)
+    torch.cuda.synchronize()
+    log(f"[decode] chunks {n_layers}x{B}x{Hkv}: worst abs error {_check(shape, q, k, v, out):.2e}")
