@@ -20,6 +20,24 @@ constexpr int kMaxLayers = 48;
 constexpr int kScoreTile = 256;
 constexpr int kScoreMaxGrid = 1024;
 
+// Share weights of the older : newer workgroup of each CU when two run on it (workgroups w
+// and w + grid/2): the wave arbiter favours the older one, so equal shares leave the newer
+// one finishing last.  Chosen per launch by the launcher from per-workgroup timestamps and
+// interleaved timings on MI355X: where every wave of the register-row stats pass owns the
+// same number of 32-row blocks (a multiple of 4 blocks), 3 : 2 for the stats pass and 4 : 3
+// for the finish pass; otherwise 9 : 7 and 15 : 13.  The stats weights also number the
+// statistics partials, so both passes of a call use the same ones.
+struct SplitWeights {
+  int stats_old, stats_new, finish_old, finish_new;
+};
+constexpr SplitWeights kWeightsBalanced = {3, 2, 4, 3};
+constexpr SplitWeights kWeightsDefault = {9, 7, 15, 13};
+// The most skewed stats weights any launch uses (the slot bound below depends on them).
+constexpr int kMaxSkewOld = 3, kMaxSkewNew = 2;
+static_assert(kWeightsBalanced.stats_old * kMaxSkewNew <= kMaxSkewOld * kWeightsBalanced.stats_new &&
+                  kWeightsDefault.stats_old * kMaxSkewNew <= kMaxSkewOld * kWeightsDefault.stats_new,
+              "stats weights within the slot bound");
+
 struct ScoreArgs {
   const uint16_t* k[kMaxLayers];
   const uint16_t* q[kMaxLayers];
@@ -35,25 +53,18 @@ struct ScoreArgs {
   int obs_pad;          // observation rows per unit rounded up to 32 (launch-wide)
   int slots;            // statistics slots per unit (set by the launcher)
   int paired;           // two workgroups per CU, w and w + grid/2 (set by the launcher)
+  SplitWeights weights; // older : newer share weights of a pair (set by the launcher)
   int mean;             // 1: mean of the observation rows' attention weights, 0: max
   float scale_log2;     // log2(e) / sqrt(head_dim)
 };
 
-// Share weights of the older : newer workgroup of each CU when two run on it (workgroups w
-// and w + grid/2): the wave arbiter favours the older one, so equal shares leave the newer
-// one finishing last.  Measured on MI355X per pass from per-workgroup timestamps.  The
-// stats weights also number the statistics partials, so both passes and both stats
-// implementations use them.
-constexpr int kStatsWeightOld = 9, kStatsWeightNew = 7;
-constexpr int kFinishWeightOld = 15, kFinishWeightNew = 13;
-
 // Statistics slots per unit for a launch of n_layers layers (the workspace is sized from
 // this): one per workgroup that can share a unit, never more than the unit's tiles.  The
-// smallest stats share is 2 B / (A + B) of the mean (weights A : B), so at most
-// grid (A + B) / (2 B) / units + 2 workgroups meet one unit.
+// smallest stats share is at least 2 B / (A + B) of the mean (weights A : B up to the
+// most skewed), so at most grid (A + B) / (2 B) / units + 2 workgroups meet one unit.
 inline int score_slots(int capacity, int n_layers, int n_kv_heads) {
   const int tiles = (capacity + kScoreTile - 1) / kScoreTile;
-  const int sharing = kScoreMaxGrid * (kStatsWeightOld + kStatsWeightNew) / (2 * kStatsWeightNew) /
+  const int sharing = kScoreMaxGrid * (kMaxSkewOld + kMaxSkewNew) / (2 * kMaxSkewNew) /
                           (n_layers * n_kv_heads) + 2;
   return tiles < sharing ? tiles : sharing;
 }

@@ -528,10 +528,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
   sp.H = sp.G / 2;
   // Partial slots are numbered by the stats pass's split in both passes.
   Split ss = sp;
-  ss.A = weighted ? kStatsWeightOld : 1;
-  ss.B = weighted ? kStatsWeightNew : 1;
-  sp.A = weighted ? (FINISH ? kFinishWeightOld : kStatsWeightOld) : 1;
-  sp.B = weighted ? (FINISH ? kFinishWeightNew : kStatsWeightNew) : 1;
+  ss.A = weighted ? a.weights.stats_old : 1;
+  ss.B = weighted ? a.weights.stats_new : 1;
+  sp.A = weighted ? (FINISH ? a.weights.finish_old : a.weights.stats_old) : 1;
+  sp.B = weighted ? (FINISH ? a.weights.finish_new : a.weights.stats_new) : 1;
   const long long c0 = sp.begin(w);
   const long long c1 = sp.begin(w + 1);
   Cursor cur = locate(a, c0, T);
@@ -597,6 +597,7 @@ hipError_t launch_d(ScoreArgs a, int n_layers, hipStream_t s) {
   a.n_layers = n_layers;
   a.slots = score_slots(a.capacity, n_layers, a.n_kv_heads);
   a.paired = std::min(per_cu, per_cu_stats) == 2 ? 1 : 0;
+  a.weights = qs_stats && (a.obs_pad / 32) % kWaves == 0 ? kWeightsBalanced : kWeightsDefault;
   if (qs_stats) {
     e = launch_qs_stats(a, D, grid, s);
     if (e != hipSuccess) return e;

@@ -374,8 +374,8 @@ __device__ inline void qs_stats_body(const ScoreArgs& a, uint8_t* ring) {
   if (w >= sp.G) return;
   const bool weighted = a.paired && sp.G == static_cast<int>(gridDim.x) && (sp.G & 1) == 0 && sp.N >= 2LL * sp.G;
   sp.H = sp.G / 2;
-  sp.A = weighted ? kStatsWeightOld : 1;
-  sp.B = weighted ? kStatsWeightNew : 1;
+  sp.A = weighted ? a.weights.stats_old : 1;
+  sp.B = weighted ? a.weights.stats_new : 1;
   const long long c0 = sp.begin(w);
   const long long c1 = sp.begin(w + 1);
   Cursor cur = locate(a, c0, T);
