@@ -357,7 +357,9 @@ def main():
     # The committed counter summary holds for the workload as named, max aggregation.
     as_named = args.window is None and args.beacons is None and args.budget is None and args.aggregation == "max"
     traffic = score_traffic(w.name) if dom == "score" and as_named else None
-    stats_kernel = ("qs_stats_kernel<D,BPW>" if w.group * w.window + w.nb_max <= 256 else "score_kernel<D,false>")
+    obs_pad = -(-(w.group * w.window + w.nb_max) // 32) * 32
+    stats_kernel = ("qs_stats_kernel<D,BPW>" if obs_pad <= 256 else
+                    "qs_stats_kernel_wide<D,3>" if obs_pad <= 384 else "score_kernel<D,false>")
     roof = {"kernel": {"score": f"{stats_kernel} (stats) + score_kernel<D,true> (finish): one bkv_score call",
                        "select": "select_topk_kernel (bkv_select_topk)",
                        "compact": "compact_kernel (bkv_compact)",
