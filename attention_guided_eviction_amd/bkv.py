@@ -32,7 +32,7 @@ AGG_MAX, AGG_MEAN = 0, 1
 AGGREGATIONS = {"max": AGG_MAX, "mean": AGG_MEAN}
 BEACON_FPS, BEACON_INITIAL = 0, 1
 BEACON_POLICIES = {"fps": BEACON_FPS, "initial": BEACON_INITIAL}
-MAX_POOL = 768
+MAX_POOL = 16384
 
 EXPORTS = ["bkv_status_string", "bkv_version", "bkv_last_error", "bkv_update_beacons", "bkv_update_beacons_policy",
            "bkv_score_workspace_bytes",

@@ -93,7 +93,9 @@ struct CompactArgs {
 };
 
 // ---- beacons -----------------------------------------------------------------------------
-constexpr int kFpsThreads = 1024;   // one pool row per thread: pools up to 1024 rows
+constexpr int kFpsThreads = 1024;       // workgroup of both beacon kernels
+constexpr int kFpsRegisterPool = 768;   // pools up to this many rows: one row per thread, in registers
+constexpr int kFpsPoolRowsPerThread = 16;   // larger pools: up to 16 rows per thread, streamed
 
 struct FpsArgs {
   const uint16_t* beacons_in[kMaxLayers];

@@ -11,6 +11,8 @@
 // takes the dot product of its row with it by v_dot2_f32_bf16 with the row in SGPRs: no
 // cross-lane reduction per row.  Each thread keeps its row's distance to the nearest
 // chosen row; a block-wide max of (distance, lowest index on ties) names the next pick.
+#include <mutex>
+
 #include "bkv_internal.h"
 
 namespace bkv {
@@ -150,6 +152,129 @@ __global__ __launch_bounds__(kFpsThreads) void fps_kernel(const FpsArgs a) {
   if (tid == 0) a.n_out[layer][bh] = a.nb_max;
 }
 
+// Pools larger than the register-resident kernel takes (the Naive FPS of Figure 7: every
+// query of the history in one pool): 1024 threads per unit, thread t handles pool rows
+// t, t + 1024, ...  Each row's inverse norm and distance to its nearest chosen row sit in
+// LDS (a chosen row's distance is set to -1, which no distance reaches), and each pick
+// streams the rows again from their read-only sources.  Picks, distances and the tie rule
+// (lowest pool index) are those of fps_kernel.
+template <int D>
+__global__ __launch_bounds__(kFpsThreads) void fps_pool_kernel(const FpsArgs a) {
+  constexpr int W = D / 2;
+  extern __shared__ float2 row_s[];   // [pool rows]: (inverse norm, distance to the chosen set)
+  __shared__ unsigned best_v[2][kWaves];
+  __shared__ int best_i[2][kWaves];
+  const int u = blockIdx.x;
+  const int per_layer = a.batch * a.n_kv_heads;
+  const int layer = u / per_layer;
+  const int bh = u - layer * per_layer;
+  const int b = bh / a.n_kv_heads;
+  const int h = bh - b * a.n_kv_heads;
+  int c_in = a.nb_max > 0 ? a.n_in[layer][bh] : 0;
+  c_in = c_in < 0 ? 0 : (c_in > a.nb_max ? a.nb_max : c_in);
+  const int P = c_in + a.group * a.t_new;
+  const uint16_t* bin = a.beacons_in[layer] + static_cast<size_t>(bh) * a.nb_max * D;
+  const uint16_t* qn = a.q_new[layer];
+  uint16_t* out = a.beacons_out[layer] + static_cast<size_t>(bh) * a.nb_max * D;
+  const int tid = threadIdx.x;
+
+  auto row_ptr = [&](int p) -> const uint16_t* {
+    if (p < c_in) return bin + static_cast<size_t>(p) * D;
+    const int qi = p - c_in;
+    const int r = qi / a.t_new;
+    const int t = qi - r * a.t_new;
+    return qn + ((static_cast<size_t>(b) * a.n_q_heads + h * a.group + r) * a.q_len + (a.q_len - a.t_new + t)) * D;
+  };
+
+  if (P <= a.nb_max) {  // everything fits: keep the pool as is
+    constexpr int kChunks = D / 8;
+    for (int e = tid; e < P * kChunks; e += kFpsThreads) {
+      const int p = e / kChunks;
+      const int cc = e - p * kChunks;
+      *reinterpret_cast<uint4*>(out + static_cast<size_t>(p) * D + cc * 8) =
+          *reinterpret_cast<const uint4*>(row_ptr(p) + cc * 8);
+    }
+    if (tid == 0) a.n_out[layer][bh] = P;
+    return;
+  }
+
+  for (int p = tid; p < P; p += kFpsThreads) {
+    const uint4* src = reinterpret_cast<const uint4*>(row_ptr(p));
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < W / 4; ++i) {
+      const uint4 v = src[i];
+      ss = dot2(v.x, v.x, ss);
+      ss = dot2(v.y, v.y, ss);
+      ss = dot2(v.z, v.z, ss);
+      ss = dot2(v.w, v.w, ss);
+    }
+    row_s[p] = make_float2(1.0f / fmaxf(sqrtf(ss), 1e-30f), 2.f);
+  }
+  __syncthreads();
+
+  int cur = 0;
+  for (int t = 0; t < a.nb_max; ++t) {
+    if ((cur & (kFpsThreads - 1)) == tid) {   // the pick's owner writes it out and leaves the candidates
+      const uint4* src = reinterpret_cast<const uint4*>(row_ptr(cur));
+      uint4* dst = reinterpret_cast<uint4*>(out + static_cast<size_t>(t) * D);
+#pragma unroll
+      for (int i = 0; i < W / 4; ++i) dst[i] = src[i];
+      row_s[cur].y = -1.f;
+    }
+    if (t == a.nb_max - 1) break;
+    const const_u32 y = (const_u32)(row_ptr(cur));   // uniform: scalar loads
+    const float ic = row_s[cur].x;
+    unsigned best = 0u;   // distance bits + 1 of this thread's farthest candidate; 0: none
+    int best_p = 0;
+    for (int p = tid; p < P; p += kFpsThreads) {   // ascending: strict > keeps the lowest index
+      const uint4* src = reinterpret_cast<const uint4*>(row_ptr(p));
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < W / 4; ++i) {
+        const uint4 v = src[i];
+        acc[0] = dot2(v.x, y[4 * i], acc[0]);
+        acc[1] = dot2(v.y, y[4 * i + 1], acc[1]);
+        acc[2] = dot2(v.z, y[4 * i + 2], acc[2]);
+        acc[3] = dot2(v.w, y[4 * i + 3], acc[3]);
+      }
+      const float dt = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+      const float2 rs = row_s[p];
+      float d = 1.0f - dt * rs.x * ic;
+      d = fminf(fmaxf(d, 0.f), 2.f);
+      if (rs.y >= 0.f) {   // still a candidate
+        const float m = fminf(rs.y, d);   // the initial 2 is the largest distance
+        row_s[p].y = m;
+        const unsigned key = __float_as_uint(m) + 1u;
+        if (key > best) {
+          best = key;
+          best_p = p;
+        }
+      }
+    }
+    // workgroup max of (distance, lowest pool index on ties)
+    const unsigned wmax = wave_umax(best);
+    const unsigned lowest = ~wave_umax(best == wmax ? ~static_cast<unsigned>(best_p) : 0u);
+    if ((tid & 63) == 0) {
+      best_v[t & 1][tid >> 6] = wmax;
+      best_i[t & 1][tid >> 6] = static_cast<int>(lowest);
+    }
+    __syncthreads();
+    unsigned bv = best_v[t & 1][0];
+    int bi = best_i[t & 1][0];
+    for (int w = 1; w < kWaves; ++w) {
+      const unsigned ov = best_v[t & 1][w];
+      const int oi = best_i[t & 1][w];
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    cur = __builtin_amdgcn_readfirstlane(bi);
+  }
+  if (tid == 0) a.n_out[layer][bh] = a.nb_max;
+}
+
 // Table 3's Initial+Recent baseline keeps the earliest queries instead: the live rows stay
 // in place and the new queries fill the free slots in time order (all heads of a step, in
 // head order, before the next step); once full the set never changes.  A plain copy of
@@ -200,8 +325,27 @@ hipError_t launch_initial(const FpsArgs& a, int n_layers, int head_dim, hipStrea
 }
 
 hipError_t launch_fps(const FpsArgs& a, int n_layers, int head_dim, int pool_max, hipStream_t s) {
-  if (pool_max > kFpsThreads) return hipErrorInvalidValue;   // rejected by the host beforehand
+  if (pool_max > kFpsThreads * kFpsPoolRowsPerThread) return hipErrorInvalidValue;   // rejected by the host beforehand
   const unsigned grid = static_cast<unsigned>(n_layers) * a.batch * a.n_kv_heads;
+  if (pool_max > kFpsRegisterPool) {
+    static std::once_flag once;
+    static hipError_t attr_err = hipSuccess;
+    std::call_once(once, [] {
+      const int lds = kFpsThreads * kFpsPoolRowsPerThread * static_cast<int>(sizeof(float2));
+      attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&fps_pool_kernel<128>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+      if (attr_err == hipSuccess)
+        attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&fps_pool_kernel<64>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    });
+    if (attr_err != hipSuccess) return note_hip_error(attr_err, "fps: hipFuncSetAttribute");
+    const size_t lds = static_cast<size_t>(pool_max) * sizeof(float2);
+    if (head_dim == 128)
+      hipLaunchKernelGGL(fps_pool_kernel<128>, dim3(grid), dim3(kFpsThreads), lds, s, a);
+    else
+      hipLaunchKernelGGL(fps_pool_kernel<64>, dim3(grid), dim3(kFpsThreads), lds, s, a);
+    return note_hip_error(hipGetLastError(), "fps: launch pool kernel");
+  }
   const int threads = pool_max < 64 ? 64 : (pool_max + 63) / 64 * 64;
   if (head_dim == 128)
     hipLaunchKernelGGL(fps_kernel<128>, dim3(grid), dim3(threads), 0, s, a);

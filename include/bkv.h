@@ -88,8 +88,9 @@ typedef struct bkv_shape {
 /* Largest number of observation rows (n_q_heads/n_kv_heads * window + nb_max) that
  * bkv_score / bkv_compress accept. */
 #define BKV_MAX_OBS 512
-/* Largest beacon pool (nb_max + n_q_heads/n_kv_heads * t_new) bkv_update_beacons accepts. */
-#define BKV_MAX_POOL 768
+/* Largest beacon pool (nb_max + n_q_heads/n_kv_heads * t_new) bkv_update_beacons accepts
+ * (pools above 768 rows, e.g. a whole query history, take a slower streaming kernel). */
+#define BKV_MAX_POOL 16384
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* bkv_status_string(bkv_status status);

@@ -143,7 +143,7 @@ def test_update_beacons_rejects():
     f = lib.bkv_update_beacons
     assert f(ctypes.byref(s), bi, ni, 0, qn, 128, 128, bo, no, None) == bkv.BKV_EINVAL       # nb_max < 1
     assert f(ctypes.byref(s), bi, ni, 16, qn, 128, 129, bo, no, None) == bkv.BKV_EINVAL     # t_new > q_len
-    assert f(ctypes.byref(s), bi, ni, 16, qn, 256, 256, bo, no, None) == bkv.BKV_EUNSUPPORTED  # pool 16+4*256
+    assert f(ctypes.byref(s), bi, ni, 16, qn, 4093, 4093, bo, no, None) == bkv.BKV_EUNSUPPORTED  # pool 16+4*4093
     assert f(ctypes.byref(s), bi, ni, 16, qn, 128, 128, bi, no, None) == bkv.BKV_EALIAS
     assert f(ctypes.byref(s), bi, ni, 16, qn, 128, 128, bo, ni, None) == bkv.BKV_EALIAS
     assert f(ctypes.byref(s), bi, ni, 16, qn, 128, 128, qn, no, None) == bkv.BKV_EALIAS
@@ -178,14 +178,14 @@ def test_update_beacons_policy_rejects_unknown_policy_and_keeps_fps_limits():
     lib = bkv.load()
     s = shape()
 
-    def call(policy, t_new=8, nb_max=16):
+    def call(policy, t_new=8, nb_max=16, q_len=200):
         return lib.bkv_update_beacons_policy(ctypes.byref(s), arr(FAKE + (1 << 36)), arr(FAKE + (2 << 36)), nb_max,
-                                             arr(FAKE + (3 << 36)), 200, t_new, policy, arr(FAKE + (4 << 36)),
+                                             arr(FAKE + (3 << 36)), q_len, t_new, policy, arr(FAKE + (4 << 36)),
                                              arr(FAKE + (5 << 36)), None)
 
     assert call(2) == bkv.BKV_EINVAL
-    # continual FPS is limited to BKV_MAX_POOL candidates; 16 + 4 * 200 > 768
-    assert call(bkv.BEACON_FPS, t_new=200) == bkv.BKV_EUNSUPPORTED
+    # continual FPS is limited to BKV_MAX_POOL candidates; 16 + 4 * 4093 > 16384
+    assert call(bkv.BEACON_FPS, t_new=4093, q_len=4093) == bkv.BKV_EUNSUPPORTED
     assert call(bkv.BEACON_INITIAL, t_new=201) == bkv.BKV_EINVAL                  # t_new > q_len
 
 
