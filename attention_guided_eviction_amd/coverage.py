@@ -1,7 +1,7 @@
 """Beacon coverage of future queries: how close the kept query set stays to the queries
 decoding will issue later (BeaconKV page, Figure 6 (a): maximum cosine similarity to
 future decoding-step queries under different past-query selections; Figure 7: continual
-FPS; Table 3: Initial+Recent).
+versus naive FPS; Table 3: Initial+Recent).
 
 The beacon sets are built on the GPU by the library's beacon update, chunk after chunk of a
 query stream; the similarity readout is a small evaluation, not part of the compression
@@ -56,7 +56,8 @@ def max_cosine(future: torch.Tensor, sets: torch.Tensor, counts: torch.Tensor) -
 def coverage(w, units: List[Tuple[int, int, int]], steps: int, future: int, chunk: int, window: int, nb_max: int,
              device="cuda") -> Dict[str, Dict[str, float]]:
     """Mean max-cosine coverage of the held-out queries by: the continual-FPS beacons, the
-    initial-query beacons, and the recent window alone; split into plan revisits and the
+    initial-query beacons, naive FPS over the whole history in one pool (when the history
+    fits the largest pool), and the recent window alone; split into plan revisits and the
     rest."""
     from synth.stream import query_stream
     qs, cids = [], []
@@ -72,9 +73,11 @@ def coverage(w, units: List[Tuple[int, int, int]], steps: int, future: int, chun
     sets = {}
     for policy in ("fps", "initial"):
         sets[policy] = beacon_stream(past.contiguous(), nb_max, chunk, policy)
+    if G * steps <= bkv.MAX_POOL:   # Figure 7's naive FPS: one pick over the whole history
+        sets["naive_fps"] = beacon_stream(past.contiguous(), nb_max, steps, "fps")
     recent = past[:, :, steps - window:].reshape(U, G * window, D)
     sets["recent"] = (recent, torch.full((U,), G * window, dtype=torch.int32, device=device))
-    for policy in ("fps", "initial"):
+    for policy in [k for k in ("fps", "initial", "naive_fps") if k in sets]:
         b, n = sets[policy]
         sets[policy + "+recent"] = (torch.cat([recent, b], dim=1), n + G * window)
     out = {}
@@ -90,7 +93,7 @@ def main():
     p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     p.add_argument("--workload", default="qwen14b_64k")
     p.add_argument("--units", type=int, default=8)
-    p.add_argument("--steps", type=int, default=4096)
+    p.add_argument("--steps", type=int, default=3200)
     p.add_argument("--future", type=int, default=512)
     p.add_argument("--chunk", type=int, default=128)
     args = p.parse_args()
