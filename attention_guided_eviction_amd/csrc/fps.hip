@@ -3,8 +3,9 @@
 // global query clusters without keeping the query history; Figure 4 (a): cosine
 // similarity between queries).
 //
-// One workgroup per unit, one thread per pool row (the workgroup is the largest pool
-// rounded up to whole waves, so two units share a CU on the largest workloads); thread p
+// Pools of up to 768 rows (continual updates): one workgroup per unit, one thread per pool
+// row (the workgroup is the largest pool rounded up to whole waves, so two units share a CU
+// on the largest workloads); larger pools take fps_pool_kernel below.  Thread p
 // holds pool row p (live beacons, then the group's new queries head-major in time order)
 // in registers as packed bf16 pairs, with its inverse norm.  A pick is uniform across the workgroup, so every wave reads the
 // picked row straight from its (read-only) source through scalar loads and each thread
