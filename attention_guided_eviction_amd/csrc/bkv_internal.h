@@ -52,8 +52,10 @@ struct ScoreArgs {
   int q_len, window, nb_max;
   int obs_pad;          // observation rows per unit rounded up to 32 (launch-wide)
   int slots;            // statistics slots per unit (set by the launcher)
-  int paired;           // two workgroups per CU, w and w + grid/2 (set by the launcher)
-  SplitWeights weights; // older : newer share weights of a pair (set by the launcher)
+  int stats_grid;       // workgroups of the stats pass, whose split numbers the partials
+  int paired;           // stats pass: two workgroups per CU, w and w + grid/2
+  int finish_paired;    // finish pass: the same on its own grid
+  SplitWeights weights; // older : newer share weights of a pair (all set by the launcher)
   int mean;             // 1: mean of the observation rows' attention weights, 0: max
   float scale_log2;     // log2(e) / sqrt(head_dim)
 };

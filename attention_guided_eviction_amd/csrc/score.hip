@@ -42,7 +42,7 @@ namespace {
 // reads of 16 consecutive rows at one chunk then touch 16 different slots, i.e. all 64
 // banks once, with no padding.  Each thread issues its loads in batches of 8 before
 // waiting, so staging costs about one memory latency per batch.
-template <int D>
+template <int D, int NT = kThreads>
 __device__ inline void stage_queries(const ScoreArgs& a, const UnitInfo& ui, uint8_t* qs) {
   constexpr int kChunks = D / 8;
   constexpr int kBatch = 8;
@@ -50,11 +50,11 @@ __device__ inline void stage_queries(const ScoreArgs& a, const UnitInfo& ui, uin
   const uint16_t* q = a.q[ui.layer];
   const uint16_t* bc = a.nb_max > 0 ? a.beacons[ui.layer] : nullptr;
   const int total = ui.nqb * 32 * kChunks;
-  for (int c0 = threadIdx.x; c0 < total; c0 += kBatch * kThreads) {
+  for (int c0 = threadIdx.x; c0 < total; c0 += kBatch * NT) {
     uint4 v[kBatch];
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
-      const int c = c0 + j * kThreads;
+      const int c = c0 + j * NT;
       const int r = c / kChunks;
       const int cc = c - r * kChunks;
       v[j] = make_uint4(0, 0, 0, 0);
@@ -72,7 +72,7 @@ __device__ inline void stage_queries(const ScoreArgs& a, const UnitInfo& ui, uin
     }
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
-      const int c = c0 + j * kThreads;
+      const int c = c0 + j * NT;
       const int r = c / kChunks;
       const int cc = c - r * kChunks;
       if (c < total) *reinterpret_cast<uint4*>(qs + r * (D * 2) + ((cc ^ (r & (kChunks - 1))) * 16)) = v[j];
@@ -509,6 +509,100 @@ __device__ void finish_segment(const ScoreArgs& a, const UnitInfo& ui, int tile0
   __syncthreads();   // LDS is restaged by the next segment
 }
 
+// Finish pass for observation sets whose staged rows leave room for one workgroup per CU
+// (over 256 rows): one workgroup of 8 waves per CU, so every SIMD still runs two waves on
+// one LDS copy of the rows.  The waves take the segment's 64-key items from an LDS counter
+// as they free up, so no wave waits on a slower partner at the end of the share.
+constexpr int kThreads8 = 512;
+
+template <int D, bool MEAN>
+__device__ void finish_segment8(const ScoreArgs& a, const UnitInfo& ui, int tile0, int ntile, const float* pm0,
+                                const float* pz0, int n_part, uint8_t* smem) {
+  Smem<D> sm(smem, a.obs_pad);
+  int* next_item = reinterpret_cast<int*>(sm.nlse + a.obs_pad);
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const uint16_t* kp = a.k[ui.layer] + (static_cast<size_t>(ui.b) * a.n_kv_heads + ui.h) * a.capacity * D;
+  float* sp = a.scores[ui.layer] + (static_cast<size_t>(ui.b) * a.n_kv_heads + ui.h) * a.capacity;
+  const int n_items = ntile * (kScoreTile / 64);
+  const int key0 = tile0 * kScoreTile;
+  int item = wave;   // the first item of each wave is fixed, so its keys load before staging
+  KeyFrag<D> kf;
+  if (item < n_items) load_keys<D>(kp, key0 + item * 64, ui.L, kf);
+  stage_queries<D, kThreads8>(a, ui, sm.qs);
+  for (int i = threadIdx.x; i < ui.nqb * 32; i += kThreads8) {
+    float M = kNegInf, Z = 0.f;
+    for (int s0 = 0; s0 < n_part; s0 += 8) {
+      float pm[8], pz[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bool use = s0 + j < n_part;
+        const size_t o = static_cast<size_t>(s0 + j) * a.obs_pad + i;
+        pm[j] = use ? pm0[o] : kNegInf;
+        pz[j] = use ? pz0[o] : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) merge_stats(M, Z, pm[j], pz[j]);
+    }
+    sm.nlse[i] = (i < ui.n_obs && Z > 0.f) ? -(M + log2f(Z)) / a.scale_log2 : kNegInf;
+  }
+  if (threadIdx.x == 0) *next_item = kThreads8 / 64;
+  __syncthreads();
+  while (item < n_items) {
+    const int kbase = key0 + item * 64;
+    if (kbase < ui.L) {
+      float v = kNegInf;
+      if (ui.nqb > 0) v = finish_tile<D, MEAN>(kf, sm.qs, sm.nlse, ui.nqb, a.scale_log2);
+      const int key = kbase + lane;
+      if (key < ui.L) sp[key] = ui.n_obs > 0 ? (MEAN ? v / static_cast<float>(ui.n_obs) : exp2f(a.scale_log2 * v)) : 0.f;
+    }
+    int nx = 0;
+    if (lane == 0) nx = atomicAdd(next_item, 1);
+    item = __builtin_amdgcn_readfirstlane(nx);
+    if (item < n_items) load_keys<D>(kp, key0 + item * 64, ui.L, kf);
+  }
+  __syncthreads();   // LDS is restaged by the next segment
+}
+
+template <int D, bool MEAN>
+__global__ __launch_bounds__(kThreads8) __attribute__((amdgpu_waves_per_eu(2, 2))) void finish8_kernel(const ScoreArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int w = static_cast<int>(blockIdx.x);
+  const int T = layer_tiles(a);
+  const long long N = static_cast<long long>(T) * a.n_layers;
+  // the partials are numbered by the stats pass's split
+  Split ss;
+  ss.N = N;
+  ss.G = static_cast<int>(N < a.stats_grid ? N : a.stats_grid);
+  ss.H = ss.G / 2;
+  const bool weighted = a.paired && ss.G == a.stats_grid && (ss.G & 1) == 0 && N >= 2LL * ss.G;
+  ss.A = weighted ? a.weights.stats_old : 1;
+  ss.B = weighted ? a.weights.stats_new : 1;
+  Split sp;
+  sp.N = N;
+  sp.G = static_cast<int>(N < gridDim.x ? N : gridDim.x);
+  sp.H = sp.G / 2;
+  sp.A = sp.B = 1;
+  if (w >= sp.G) return;
+  const long long c0 = sp.begin(w);
+  const long long c1 = sp.begin(w + 1);
+  Cursor cur = locate(a, c0, T);
+  long long c = c0;
+  for (;;) {
+    const long long left = c1 - c;
+    const int n = static_cast<int>(left < cur.nt - cur.tile ? left : cur.nt - cur.tile);
+    const long long first = c - cur.tile;
+    const int w0 = ss.owner(first);
+    const UnitInfo ui = unit_info(a, cur.u);
+    const size_t unit_part = static_cast<size_t>(cur.u) * a.slots * a.obs_pad;
+    int n_part = ss.owner(first + cur.nt - 1) - w0 + 1;
+    n_part = n_part < a.slots ? n_part : a.slots;
+    finish_segment8<D, MEAN>(a, ui, cur.tile, n, a.part_m + unit_part, a.part_z + unit_part, n_part, smem);
+    c += n;
+    if (c >= c1 || !next_unit(a, cur)) break;
+  }
+}
+
 // ---- kernels ----------------------------------------------------------------------------
 
 
@@ -517,21 +611,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int w = static_cast<int>(blockIdx.x);
   const int T = layer_tiles(a);
-  Split sp;
-  sp.N = static_cast<long long>(T) * a.n_layers;
+  const long long N = static_cast<long long>(T) * a.n_layers;
+  // Partial slots are numbered by the stats pass's split (on its own grid) in both passes.
   // With fewer tiles than workgroups only the first N take part, so every share holds at
-  // least one tile and a unit's shares are consecutive workgroups.
-  sp.G = static_cast<int>(sp.N < gridDim.x ? sp.N : gridDim.x);
+  // least one tile and a unit's shares are consecutive workgroups.  Weighted shares only
+  // where the pairs are real and every share keeps two tiles or more.
+  Split ss;
+  ss.N = N;
+  ss.G = static_cast<int>(N < a.stats_grid ? N : a.stats_grid);
+  ss.H = ss.G / 2;
+  const bool s_weighted = a.paired && ss.G == a.stats_grid && (ss.G & 1) == 0 && N >= 2LL * ss.G;
+  ss.A = s_weighted ? a.weights.stats_old : 1;
+  ss.B = s_weighted ? a.weights.stats_new : 1;
+  Split sp = ss;
+  if (FINISH) {
+    sp.G = static_cast<int>(N < gridDim.x ? N : gridDim.x);
+    sp.H = sp.G / 2;
+    const bool f_weighted =
+        a.finish_paired && sp.G == static_cast<int>(gridDim.x) && (sp.G & 1) == 0 && N >= 2LL * sp.G;
+    sp.A = f_weighted ? a.weights.finish_old : 1;
+    sp.B = f_weighted ? a.weights.finish_new : 1;
+  }
   if (w >= sp.G) return;
-  // Weighted shares only where the pairs are real and every share keeps two tiles or more.
-  const bool weighted = a.paired && sp.G == static_cast<int>(gridDim.x) && (sp.G & 1) == 0 && sp.N >= 2LL * sp.G;
-  sp.H = sp.G / 2;
-  // Partial slots are numbered by the stats pass's split in both passes.
-  Split ss = sp;
-  ss.A = weighted ? a.weights.stats_old : 1;
-  ss.B = weighted ? a.weights.stats_new : 1;
-  sp.A = weighted ? (FINISH ? a.weights.finish_old : a.weights.stats_old) : 1;
-  sp.B = weighted ? (FINISH ? a.weights.finish_new : a.weights.stats_new) : 1;
   const long long c0 = sp.begin(w);
   const long long c1 = sp.begin(w + 1);
   Cursor cur = locate(a, c0, T);
@@ -573,6 +674,12 @@ hipError_t launch_d(ScoreArgs a, int n_layers, hipStream_t s) {
     if (attr_err == hipSuccess)
       attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&score_kernel<D, true, true>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (attr_err == hipSuccess)
+      attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&finish8_kernel<D, true>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (attr_err == hipSuccess)
+      attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&finish8_kernel<D, false>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   });
   if (attr_err != hipSuccess) return note_hip_error(attr_err, "score: hipFuncSetAttribute");
   const size_t lds = lds_bytes(D, a.obs_pad);
@@ -591,12 +698,17 @@ hipError_t launch_d(ScoreArgs a, int n_layers, hipStream_t s) {
   else
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_stats, score_kernel<D, false>, kThreads, lds);
   if (e != hipSuccess) return note_hip_error(e, "score: hipOccupancyMaxActiveBlocksPerMultiprocessor");
-  // Every workgroup resident at once: the shares are equal, so none waits for a slot.  Both
-  // passes run on the same grid, which fixes the numbering of the statistics partials.
-  const int grid = std::min(kScoreMaxGrid, std::max(1, std::min(per_cu, per_cu_stats)) * cus);
+  // Every workgroup resident at once (at most two per CU): the shares are static, so none
+  // waits for a slot.  Each pass runs on its own grid; the stats grid numbers the partials.
+  per_cu = std::max(1, std::min(2, per_cu));
+  per_cu_stats = std::max(1, std::min(2, per_cu_stats));
+  const int grid = std::min(kScoreMaxGrid, per_cu_stats * cus);
+  const int grid_finish = std::min(kScoreMaxGrid, per_cu * cus);
   a.n_layers = n_layers;
   a.slots = score_slots(a.capacity, n_layers, a.n_kv_heads);
-  a.paired = std::min(per_cu, per_cu_stats) == 2 ? 1 : 0;
+  a.stats_grid = grid;
+  a.paired = per_cu_stats == 2 ? 1 : 0;
+  a.finish_paired = per_cu == 2 ? 1 : 0;
   a.weights = qs_stats && (a.obs_pad / 32) % kWaves == 0 ? kWeightsBalanced : kWeightsDefault;
   if (qs_stats) {
     e = launch_qs_stats(a, D, grid, s);
@@ -606,10 +718,17 @@ hipError_t launch_d(ScoreArgs a, int n_layers, hipStream_t s) {
     e = hipGetLastError();
     if (e != hipSuccess) return note_hip_error(e, "score: launch score_stats");
   }
-  if (a.mean)
-    hipLaunchKernelGGL((score_kernel<D, true, true>), dim3(grid), dim3(kThreads), lds, s, a);
-  else
-    hipLaunchKernelGGL((score_kernel<D, true>), dim3(grid), dim3(kThreads), lds, s, a);
+  if (per_cu == 1) {   // one workgroup of 4 waves per CU: take the 8-wave finish instead
+    const size_t lds8 = static_cast<size_t>(a.obs_pad) * (D * 2 + sizeof(float)) + 16;
+    if (a.mean)
+      hipLaunchKernelGGL((finish8_kernel<D, true>), dim3(cus), dim3(kThreads8), lds8, s, a);
+    else
+      hipLaunchKernelGGL((finish8_kernel<D, false>), dim3(cus), dim3(kThreads8), lds8, s, a);
+  } else if (a.mean) {
+    hipLaunchKernelGGL((score_kernel<D, true, true>), dim3(grid_finish), dim3(kThreads), lds, s, a);
+  } else {
+    hipLaunchKernelGGL((score_kernel<D, true>), dim3(grid_finish), dim3(kThreads), lds, s, a);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return note_hip_error(e, "score: launch score_finish");
   return hipSuccess;
