@@ -144,10 +144,12 @@ struct DecodeArgs {
 
 // Launchers (return hipSuccess or the launch error).  n_layers <= kMaxLayers.
 hipError_t launch_score(const ScoreArgs& a, int n_layers, int head_dim, hipStream_t s);
-// Statistics pass with the observation rows in registers, for units of at most kQsMaxRows
-// padded rows: resident workgroups per CU, and one launch on `grid` workgroups (a.n_layers,
-// a.slots and a.paired set by the caller; the finish pass runs on the same grid).
+// Statistics pass with the observation rows in registers, for units of at most 512 padded
+// rows at head_dim 128 and kQsMaxRows at 64 (qs_stats_covers): resident workgroups per CU,
+// and one launch on `grid` workgroups (a.n_layers, a.slots, a.stats_grid and a.paired set
+// by the caller).
 constexpr int kQsMaxRows = 384;
+bool qs_stats_covers(int head_dim, int obs_pad);
 hipError_t qs_stats_occupancy(int head_dim, int obs_pad, int* per_cu);
 hipError_t launch_qs_stats(const ScoreArgs& a, int head_dim, int grid, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, int n_layers, hipStream_t s);

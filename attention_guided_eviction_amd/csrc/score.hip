@@ -692,7 +692,7 @@ hipError_t launch_d(ScoreArgs a, int n_layers, hipStream_t s) {
   e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, score_kernel<D, true>, kThreads, lds);
   if (e != hipSuccess) return note_hip_error(e, "score: hipOccupancyMaxActiveBlocksPerMultiprocessor");
   // The stats pass keeps the observation rows in registers where they fit.
-  const bool qs_stats = a.obs_pad <= kQsMaxRows;
+  const bool qs_stats = qs_stats_covers(D, a.obs_pad);
   if (qs_stats)
     e = qs_stats_occupancy(D, a.obs_pad, &per_cu_stats);
   else

@@ -25,16 +25,16 @@ namespace {
 constexpr int kSlots = 4;
 constexpr int kAhead = kSlots - 1;
 
-template <int D>
+template <int D, int NW>
 struct Qs {
   static constexpr int kRowBytes = 2 * D;
   static constexpr int kChunks = D / 8;                    // 16-byte chunks per key row
   static constexpr int kFragBytes = 32 * kRowBytes;        // one 32-key fragment
   static constexpr int kInstr = kFragBytes / 1024;         // 64-lane 16-byte loads per fragment
-  static constexpr int kPerWave = kInstr / kWaves;
+  static constexpr int kPerWave = kInstr / NW;
   static constexpr int kRowsPerInstr = 1024 / kRowBytes;
   static constexpr int kS = D / 16;                        // MFMA k-steps per row
-  static_assert(kPerWave >= 1 && kInstr % kWaves == 0, "fragment loads split evenly over the waves");
+  static_assert(kPerWave >= 1 && kInstr % NW == 0, "fragment loads split evenly over the waves");
 };
 
 // s_waitcnt immediate: vector memory count <= vm and LDS count <= lgkm (export count
@@ -47,9 +47,9 @@ constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 1
 // chunk p ^ (r mod kChunks) of that row, so LDS holds row r's chunk c at position
 // c ^ (r mod kChunks) (the swizzle that makes the MFMA-layout reads conflict-free) while
 // every load still covers whole key rows.
-template <int D>
+template <int D, int NW>
 __device__ inline void issue_fragment(const uint16_t* kp, int key0, int L, uint8_t* slot) {
-  using C = Qs<D>;
+  using C = Qs<D, NW>;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
 #pragma unroll
@@ -104,14 +104,14 @@ struct RowRegs {
   bf16x8 v[BPW][D / 16];
 };
 
-template <int D, int BPW>
+template <int D, int BPW, int NW>
 __device__ inline void load_rows(const ScoreArgs& a, const UnitInfo& ui, RowRegs<D, BPW>& q) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int gw = a.group * a.window;
 #pragma unroll
   for (int b = 0; b < BPW; ++b) {
-    const int r = (wave + kWaves * b) * 32 + (lane & 31);
+    const int r = (wave + NW * b) * 32 + (lane & 31);
     const uint16_t* p = nullptr;
     if (r < gw) {
       const int hq = ui.h * a.group + r / a.window;
@@ -129,10 +129,11 @@ __device__ inline void load_rows(const ScoreArgs& a, const UnitInfo& ui, RowRegs
   }
 }
 
-// Row blocks this wave owns in a unit with nqb blocks.
+// Row blocks this wave owns in a unit with nqb blocks (NW waves per workgroup).
+template <int NW>
 __device__ inline int owned_blocks(int nqb) {
   const int wave = threadIdx.x >> 6;
-  return nqb > wave ? (nqb - wave + kWaves - 1) / kWaves : 0;
+  return nqb > wave ? (nqb - wave + NW - 1) / NW : 0;
 }
 
 // ---- stats pass -------------------------------------------------------------------------
@@ -268,15 +269,15 @@ __device__ inline void stats_drain(f32x16 (&cur)[BPW], RowStat (&st)[BPW], int p
 // The fragment loop of a wave owning NB >= 1 blocks.  Two accumulator sets alternate
 // (fragment f's products in one while the other's exp2 work is done), unrolled by two so
 // that both stay in registers.
-template <int D, int BPW, int NB>
+template <int D, int BPW, int NB, int NW>
 __device__ inline void stats_loop(const uint16_t* kp, const UnitInfo& ui, int key_begin, int nf, uint8_t* ring,
                                   const RowRegs<D, BPW>& q, RowStat (&st)[BPW], float c) {
-  using C = Qs<D>;
+  using C = Qs<D, NW>;
   f32x16 A[BPW], B[BPW];
   auto step = [&](int f, f32x16(&nxt)[BPW], f32x16(&cur)[BPW]) {
     ring_wait<waitcnt_imm((kAhead - 1) * C::kPerWave, 0)>();
     const int fa = f + kAhead < nf ? f + kAhead : nf - 1;
-    issue_fragment<D>(kp, key_begin + 32 * fa, ui.L, ring + ((f + kAhead) % kSlots) * C::kFragBytes);
+    issue_fragment<D, NW>(kp, key_begin + 32 * fa, ui.L, ring + ((f + kAhead) % kSlots) * C::kFragBytes);
     KeyRegs<D> k;
     read_keys<D>(ring + (f % kSlots) * C::kFragBytes, k);
     if (f == 0) {
@@ -307,10 +308,10 @@ __device__ inline void stats_loop(const uint16_t* kp, const UnitInfo& ui, int ke
 }
 
 // Tiles tile0 .. tile0+ntile-1 of one unit -> partial statistics out_m/out_z [nqb*32].
-template <int D, int BPW>
+template <int D, int BPW, int NW>
 __device__ void qs_stats_segment(const ScoreArgs& a, const UnitInfo& ui, int tile0, int ntile, float* out_m,
                                  float* out_z, uint8_t* ring) {
-  using C = Qs<D>;
+  using C = Qs<D, NW>;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const uint16_t* kp = a.k[ui.layer] + (static_cast<size_t>(ui.b) * a.n_kv_heads + ui.h) * a.capacity * D;
@@ -319,25 +320,25 @@ __device__ void qs_stats_segment(const ScoreArgs& a, const UnitInfo& ui, int til
   const int nf = (key_end - key_begin + 31) / 32;
 #pragma unroll
   for (int f = 0; f < kAhead; ++f)
-    issue_fragment<D>(kp, key_begin + 32 * (f < nf ? f : nf - 1), ui.L, ring + f * C::kFragBytes);
+    issue_fragment<D, NW>(kp, key_begin + 32 * (f < nf ? f : nf - 1), ui.L, ring + f * C::kFragBytes);
   RowRegs<D, BPW> q;
-  load_rows<D, BPW>(a, ui, q);
-  const int nb = owned_blocks(ui.nqb);
+  load_rows<D, BPW, NW>(a, ui, q);
+  const int nb = owned_blocks<NW>(ui.nqb);
   const float c = a.scale_log2;
   RowStat st[BPW];
 #pragma unroll
   for (int b = 0; b < BPW; ++b) st[b] = RowStat{kNegInf, 0.f};
   if (nb == BPW) {
-    stats_loop<D, BPW, BPW>(kp, ui, key_begin, nf, ring, q, st, c);
+    stats_loop<D, BPW, BPW, NW>(kp, ui, key_begin, nf, ring, q, st, c);
   } else if (BPW == 3 && nb == 2) {
-    stats_loop<D, BPW, (BPW > 2 ? 2 : 1)>(kp, ui, key_begin, nf, ring, q, st, c);
+    stats_loop<D, BPW, (BPW > 2 ? 2 : 1), NW>(kp, ui, key_begin, nf, ring, q, st, c);
   } else if (nb == 1) {
-    stats_loop<D, BPW, 1>(kp, ui, key_begin, nf, ring, q, st, c);
+    stats_loop<D, BPW, 1, NW>(kp, ui, key_begin, nf, ring, q, st, c);
   } else {   // no rows: keep the workgroup's barrier count
     for (int f = 0; f < nf; ++f) {
       ring_wait<waitcnt_imm((kAhead - 1) * C::kPerWave, 0)>();
-      issue_fragment<D>(kp, key_begin + 32 * (f + kAhead < nf ? f + kAhead : nf - 1), ui.L,
-                        ring + ((f + kAhead) % kSlots) * C::kFragBytes);
+      issue_fragment<D, NW>(kp, key_begin + 32 * (f + kAhead < nf ? f + kAhead : nf - 1), ui.L,
+                            ring + ((f + kAhead) % kSlots) * C::kFragBytes);
     }
   }
   // lanes l and l ^ 32 hold the two key halves of the same row
@@ -346,7 +347,7 @@ __device__ void qs_stats_segment(const ScoreArgs& a, const UnitInfo& ui, int til
     if (b < nb) {
       float m = st[b].m, z = st[b].z;
       merge_stats(m, z, __shfl_xor(m, 32), __shfl_xor(z, 32));
-      const int row = (wave + kWaves * b) * 32 + lane;
+      const int row = (wave + NW * b) * 32 + lane;
       if (lane < 32) {
         out_m[row] = m;
         out_z[row] = z;
@@ -361,10 +362,10 @@ __device__ void qs_stats_segment(const ScoreArgs& a, const UnitInfo& ui, int til
 
 template <int D>
 constexpr size_t qs_lds_bytes() {
-  return static_cast<size_t>(kSlots) * Qs<D>::kFragBytes;
+  return static_cast<size_t>(kSlots) * 32 * 2 * D;
 }
 
-template <int D, int BPW>
+template <int D, int BPW, int NW>
 __device__ inline void qs_stats_body(const ScoreArgs& a, uint8_t* ring) {
   const int w = static_cast<int>(blockIdx.x);
   const int T = layer_tiles(a);
@@ -387,7 +388,7 @@ __device__ inline void qs_stats_body(const ScoreArgs& a, uint8_t* ring) {
     const UnitInfo ui = unit_info(a, cur.u);
     if (w - w0 < a.slots) {
       const size_t o = (static_cast<size_t>(cur.u) * a.slots + (w - w0)) * a.obs_pad;
-      qs_stats_segment<D, BPW>(a, ui, cur.tile, n, a.part_m + o, a.part_z + o, ring);
+      qs_stats_segment<D, BPW, NW>(a, ui, cur.tile, n, a.part_m + o, a.part_z + o, ring);
     }
     c += n;
     if (c >= c1 || !next_unit(a, cur)) break;
@@ -395,26 +396,44 @@ __device__ inline void qs_stats_body(const ScoreArgs& a, uint8_t* ring) {
 }
 
 // Up to two row blocks per wave fit in 256 registers (two waves per SIMD); three take one
-// wave per SIMD and its 512 registers.
+// wave per SIMD and its 512 registers.  With head_dim 128, 9 to 16 blocks instead take one
+// workgroup of 8 waves per CU (two per SIMD, up to two blocks each).
 template <int D, int BPW>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void qs_stats_kernel(const ScoreArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t ring[];
-  qs_stats_body<D, BPW>(a, ring);
+  qs_stats_body<D, BPW, kWaves>(a, ring);
 }
 
 template <int D, int BPW>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void qs_stats_kernel_wide(
     const ScoreArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t ring[];
-  qs_stats_body<D, BPW>(a, ring);
+  qs_stats_body<D, BPW, kWaves>(a, ring);
 }
 
+constexpr int kWaves8 = 8;
+
+template <int D>
+__global__ __launch_bounds__(64 * kWaves8) __attribute__((amdgpu_waves_per_eu(2, 2))) void qs_stats_kernel8(
+    const ScoreArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t ring[];
+  qs_stats_body<D, 2, kWaves8>(a, ring);
+}
+
+// Kernel of a row-block count class: 1, 2 or 3 blocks per wave of 4, or 8 waves (BPW 8).
 template <int D, int BPW>
 constexpr auto qs_kernel_of() {
-  if constexpr (BPW == 3)
+  if constexpr (BPW == 8)
+    return &qs_stats_kernel8<D>;
+  else if constexpr (BPW == 3)
     return &qs_stats_kernel_wide<D, BPW>;
   else
     return &qs_stats_kernel<D, BPW>;
+}
+
+template <int BPW>
+constexpr int threads_of() {
+  return BPW == 8 ? 64 * kWaves8 : kThreads;
 }
 
 template <int D, int BPW>
@@ -432,32 +451,39 @@ template <int D, int BPW>
 hipError_t occupancy(int* per_cu) {
   hipError_t e = prepare<D, BPW>();
   if (e != hipSuccess) return note_hip_error(e, "score: hipFuncSetAttribute");
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, qs_kernel_of<D, BPW>(), kThreads, qs_lds_bytes<D>());
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, qs_kernel_of<D, BPW>(), threads_of<BPW>(),
+                                                   qs_lds_bytes<D>());
   return note_hip_error(e, "score: hipOccupancyMaxActiveBlocksPerMultiprocessor");
 }
 
 template <int D, int BPW>
 hipError_t launch(const ScoreArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((qs_kernel_of<D, BPW>()), dim3(grid), dim3(kThreads), qs_lds_bytes<D>(), s, a);
+  hipLaunchKernelGGL((qs_kernel_of<D, BPW>()), dim3(grid), dim3(threads_of<BPW>()), qs_lds_bytes<D>(), s, a);
   return note_hip_error(hipGetLastError(), "score: launch score_stats");
 }
 
 }  // namespace
 
-// Row blocks per wave: 1, 2 or 3 (up to 128, 256 or 384 padded rows).
-static int blocks_per_wave(int obs_pad) { return (obs_pad + kWaves * 32 - 1) / (kWaves * 32); }
+// Kernel class of a row count: 1, 2 or 3 blocks per wave of a 4-wave workgroup (up to 128,
+// 256 or 384 padded rows), or, with head_dim 128, 8 waves for 257 to 512 rows.
+static int blocks_per_wave(int head_dim, int obs_pad) {
+  if (head_dim == 128 && obs_pad > kWaves * 64) return 8;
+  return (obs_pad + kWaves * 32 - 1) / (kWaves * 32);
+}
+
+bool qs_stats_covers(int head_dim, int obs_pad) { return obs_pad <= (head_dim == 128 ? 512 : kQsMaxRows); }
 
 hipError_t qs_stats_occupancy(int head_dim, int obs_pad, int* per_cu) {
-  const int bpw = blocks_per_wave(obs_pad);
-  if (head_dim == 128) return bpw == 3 ? occupancy<128, 3>(per_cu) : bpw == 2 ? occupancy<128, 2>(per_cu)
+  const int bpw = blocks_per_wave(head_dim, obs_pad);
+  if (head_dim == 128) return bpw == 8 ? occupancy<128, 8>(per_cu) : bpw == 2 ? occupancy<128, 2>(per_cu)
                                                                               : occupancy<128, 1>(per_cu);
   return bpw == 3 ? occupancy<64, 3>(per_cu) : bpw == 2 ? occupancy<64, 2>(per_cu) : occupancy<64, 1>(per_cu);
 }
 
 hipError_t launch_qs_stats(const ScoreArgs& a, int head_dim, int grid, hipStream_t s) {
-  const int bpw = blocks_per_wave(a.obs_pad);
+  const int bpw = blocks_per_wave(head_dim, a.obs_pad);
   if (head_dim == 128)
-    return bpw == 3 ? launch<128, 3>(a, grid, s) : bpw == 2 ? launch<128, 2>(a, grid, s) : launch<128, 1>(a, grid, s);
+    return bpw == 8 ? launch<128, 8>(a, grid, s) : bpw == 2 ? launch<128, 2>(a, grid, s) : launch<128, 1>(a, grid, s);
   return bpw == 3 ? launch<64, 3>(a, grid, s) : bpw == 2 ? launch<64, 2>(a, grid, s) : launch<64, 1>(a, grid, s);
 }
 

@@ -52,12 +52,20 @@ EDGE = {
     # head_dim 64 with 6 row blocks: two blocks on some waves of the register-resident stats pass
     "two_blocks_d64": WORKLOADS["tiny"].replace(n_q_heads=16, n_kv_heads=2, window=20, nb_init=16, nb_max=16,
                                                 t_new=0, capacity=900, seq_len=877, budget=300),
-    # exactly 256 observation rows (7 * 32 + 32), the most the register-resident stats pass takes
+    # exactly 256 observation rows (7 * 32 + 32), the most the 4-wave register-row stats pass takes
     "obs_256": WORKLOADS["qwen7b_16k"].replace(n_layers=1, capacity=1300, seq_len=1291, budget=400, nb_init=32,
                                                nb_max=32),
     # head_dim 64 with 11 row blocks (16 * 20 + 32 = 352 rows): three blocks on some waves
     "three_blocks_d64": WORKLOADS["tiny"].replace(n_q_heads=32, n_kv_heads=2, window=20, nb_init=32, nb_max=32,
                                                   t_new=0, capacity=1200, seq_len=1177, budget=300),
+    # head_dim 128 with 9 row blocks (7 * 32 + 64 = 288 rows): the 8-wave register-row stats
+    # pass with one wave holding two blocks and seven holding one
+    "nine_blocks": WORKLOADS["qwen7b_16k"].replace(n_layers=2, capacity=1400, seq_len=1389, budget=500, nb_init=64,
+                                                   nb_max=64),
+    # head_dim 64 with 480 rows (8 * 56 + 32): above the register-row stats pass at head_dim 64,
+    # so the LDS-staged stats pass
+    "lds_stats_d64": WORKLOADS["tiny"].replace(n_q_heads=16, n_kv_heads=2, window=56, nb_init=32, nb_max=32,
+                                               t_new=0, capacity=800, seq_len=777, budget=300),
     # window equals budget: nothing chosen by score
     "window_eq_budget": WORKLOADS["tiny"].replace(window=8, budget=8, t_new=0, capacity=400, seq_len=400),
     # more layers than one launch holds (48)
