@@ -7,21 +7,23 @@
 // where lse_i normalises row i over all valid keys.  Everything runs in the log2
 // domain: t_ij = s_ij * log2(e) and score_j = exp2(max_i(t_ij - lse2_i)).
 //
-// Two persistent kernels.  The launch's key tiles (256 keys each, unit after unit) are
-// cut into one contiguous, equal share per workgroup; a share covers the end of one unit,
-// whole units and the start of another.  Per unit piece ("segment") a workgroup stages
-// the unit's observation rows in LDS once and then walks its tiles.  No workgroup ever
-// waits for another:
+// Two persistent kernels, each on its own grid.  The launch's key tiles (256 keys each, unit
+// after unit) are cut into one contiguous share per workgroup (weighted where two
+// workgroups share a CU); a share covers the end of one unit, whole units and the start
+// of another.  Per unit piece ("segment") a workgroup stages the unit's observation rows
+// in LDS once and then walks its tiles.  No workgroup ever waits for another:
 //   score_stats   per-row running max and sum of exp2 over the segment's keys ->
 //                 one partial (m, z) per (unit, segment) and row;
 //   score_finish  merges the unit's partials into lse2 per row (in LDS), recomputes
 //                 the logits and writes exp2(max_i(t_ij - lse2_i)) for its keys.
 // Both passes are bound by the matrix and vector units rather than by HBM, so the keys
-// are simply read twice.  The segments of a unit are numbered by workgroup (the
-// workgroup holding a tile follows arithmetically from the split, see score_common.h),
-// so the finish pass finds every partial of a unit without any table.  For units of at
-// most 384 observation rows the stats pass is the register-resident one of score_qs.hip,
-// which writes the same partials.
+// are simply read twice.  The segments of a unit are numbered by stats workgroup (the
+// workgroup holding a tile follows arithmetically from the split, see score_common.h), so
+// the finish pass finds every partial of a unit without any table.  Where the rows fit in
+// registers (up to 512 padded rows at head_dim 128, 384 at 64) the stats pass is the
+// register-row one of score_qs.hip, which writes the same partials; the LDS-staged stats
+// pass here takes the rest.  Where the staged rows leave room for only one 4-wave finish
+// workgroup per CU, the 8-wave finish (finish8_kernel) runs instead.
 //
 // MFMA mapping (v_mfma_f32_32x32x16_bf16, four waves, each owning 64 keys of a tile).
 // Stats pass: A = 32 keys x 16 dims, B = 16 dims x 32 observation rows, so a lane's 16

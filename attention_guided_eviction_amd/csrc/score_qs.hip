@@ -2,13 +2,15 @@
 // and the sum of exp2 of its logits over a unit piece; BeaconKV page, Figure 5 (b), (c))
 // with the observation rows held in registers and the keys streamed through LDS.  Same
 // work split and statistics partials as the LDS-staged stats pass of score.hip, whose
-// finish pass consumes them; used when a unit has at most 12 blocks of 32 observation rows.
+// finish pass consumes them; used for up to 16 blocks of 32 observation rows at head_dim
+// 128 and up to 12 at 64.
 //
-// Per workgroup (4 waves) the observation row blocks are dealt round-robin to the waves:
-// wave w keeps blocks w, w + 4 (and w + 8) in registers for the whole unit piece.  Every wave works
-// on every 32-key fragment, so a fragment is fetched from HBM once per workgroup, by all
-// four waves together, straight into LDS (`global_load_lds_dwordx4`, no registers), into
-// a ring of kSlots slots that keeps kSlots - 1 fragments in flight.  Each 16-byte key
+// Per workgroup (NW = 4 or 8 waves) the observation row blocks are dealt round-robin to the
+// waves: wave w keeps blocks w, w + NW (and w + 2 NW) in registers for the whole unit
+// piece.  Every wave works on every 32-key fragment, so a fragment is fetched from HBM once
+// per workgroup, by all waves together, straight into LDS (`global_load_lds_dwordx4`, no
+// registers), into a ring of kSlots slots that keeps kSlots - 1 fragments in flight.  Each
+// 16-byte key
 // chunk read from LDS into the MFMA layout serves one product per owned row block.
 //
 // Ring protocol, per fragment f: every wave waits for its own loads of f (in-order
