@@ -10,8 +10,8 @@
 // piece.  Every wave works on every 32-key fragment, so a fragment is fetched from HBM once
 // per workgroup, by all waves together, straight into LDS (`global_load_lds_dwordx4`, no
 // registers), into a ring of kSlots slots that keeps kSlots - 1 fragments in flight.  Each
-// 16-byte key
-// chunk read from LDS into the MFMA layout serves one product per owned row block.
+// 16-byte key chunk read from LDS into the MFMA layout serves one product per owned row
+// block.
 //
 // Ring protocol, per fragment f: every wave waits for its own loads of f (in-order
 // vmcnt), the workgroup meets at a barrier (now all of f is in LDS and every wave is done
