@@ -229,7 +229,7 @@ hipError_t launch_d(const DecodeArgs& a, unsigned grid1, unsigned grid2, hipStre
   else if (a.chunk_keys == kDecodeMinChunk)
     hipLaunchKernelGGL((decode_partial<D, G, 1>), dim3(grid1), dim3(kThreads), 0, s, a);
   else
-    return hipErrorInvalidValue;
+    return note_hip_error(hipErrorInvalidValue, "decode: chunk size");
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return note_hip_error(e, "decode: launch partial");
   hipLaunchKernelGGL(decode_merge<D>, dim3(grid2), dim3(D), 0, s, a);
@@ -248,14 +248,15 @@ hipError_t launch_g(const DecodeArgs& a, unsigned grid1, unsigned grid2, hipStre
     case 6: return launch_d<D, 6>(a, grid1, grid2, s);
     case 7: return launch_d<D, 7>(a, grid1, grid2, s);
     case 8: return launch_d<D, 8>(a, grid1, grid2, s);
-    default: return hipErrorInvalidValue;
+    default: return note_hip_error(hipErrorInvalidValue, "decode: group size");
   }
 }
 
 }  // namespace
 
-// One partial kernel per (head_dim, group size): the per-query registers (running max, sum
-// and eight output dims) and LDS scale with the group, so small groups run more waves.
+// One partial kernel per (head_dim, group size, blocks per wave): the per-query registers
+// (running max, sum and eight output dims) and LDS scale with the group, so small groups
+// run more waves, and the chunk size follows the launch size.
 hipError_t launch_decode(const DecodeArgs& a, int n_layers, int head_dim, hipStream_t s) {
   const unsigned grid1 = static_cast<unsigned>(n_layers) * a.batch * a.n_kv_heads * a.chunks;
   const unsigned grid2 = static_cast<unsigned>(n_layers) * a.batch * a.n_q_heads;
