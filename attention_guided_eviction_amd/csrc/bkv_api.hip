@@ -14,6 +14,9 @@ namespace {
 
 constexpr size_t kAlign = 256;
 
+static_assert(BKV_MAX_POOL == kFpsThreads * kFpsPoolRowsPerThread, "pool limit of the streaming beacon kernel");
+static_assert(BKV_MAX_OBS <= 512, "observation rows the score kernels take");
+
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Multiply sizes, returning false on overflow.
