@@ -1,0 +1,96 @@
+"""Host-side model of the scorer's static work split (the arithmetic of the Split struct in
+csrc/score_common.h and of the launcher in csrc/score.hip), checked on random shapes: every
+share is non-empty and contiguous, the owner of a tile is the workgroup whose share holds
+it, and no unit is met by more stats workgroups than the statistics slots the library
+sizes its workspace for (read back through bkv_score_workspace_bytes).  A unit met by more
+would lose a partial.  CPU only."""
+import ctypes
+import random
+
+import pytest
+
+from attention_guided_eviction_amd import bkv
+
+TILE, MAX_GRID = 256, 1024
+WEIGHTS = {"balanced": (3, 2), "default": (9, 7)}   # stats weights the launcher chooses from
+
+
+class Split:
+    """Shares of N tiles over G workgroups: the first H = G/2 weigh A, the rest B."""
+
+    def __init__(self, N, G, A, B):
+        self.N, self.G, self.H, self.A, self.B = N, G, G // 2, A, B
+
+    def cum(self, w):
+        return self.A * w if w <= self.H else self.A * self.H + self.B * (w - self.H)
+
+    def begin(self, w):
+        return self.cum(w) * self.N // self.cum(self.G)
+
+    def owner(self, c):
+        x = ((c + 1) * self.cum(self.G) + self.N - 1) // self.N - 1
+        w = x // self.A if x < self.A * self.H else self.H + (x - self.A * self.H) // self.B
+        return min(w, self.G - 1)
+
+
+def stats_split(N, grid, paired, weights):
+    G = min(grid, N)
+    weighted = paired and G == grid and G % 2 == 0 and N >= 2 * G
+    A, B = weights if weighted else (1, 1)
+    return Split(N, G, A, B)
+
+
+def library_slots(n_layers, batch, n_kv_heads, capacity, obs_pad):
+    """Statistics slots per unit, read back from the workspace size (one launch)."""
+    seq = (ctypes.c_int32 * 1)()
+    s = bkv._Shape(n_layers, batch, 8 * n_kv_heads, n_kv_heads, 128, capacity, ctypes.addressof(seq))
+    window = obs_pad // 8          # G = 8: 8 * window observation rows, no beacons
+    nbytes = bkv.load().bkv_score_workspace_bytes(ctypes.byref(s), window, 0)
+    per_slot = 2 * n_layers * batch * n_kv_heads * obs_pad * 4
+    assert per_slot >= 512          # the 256-byte alignment adds less than one slot
+    return nbytes // per_slot
+
+
+def _check_random_shapes(seed):
+    """Largest (span - slots) over 60 random shapes; asserts every split property."""
+    rng = random.Random(seed)
+    worst = -(1 << 30)
+    for _ in range(60):
+        n_layers = rng.choice([1, 2, 3, 7, 28, 36, 48])
+        batch = rng.choice([1, 2, 3, 5, 8, 64])
+        hkv = rng.choice([1, 2, 4, 8])
+        cap = rng.choice([256, 257, 1000, 4096, 16384, 65536])
+        if n_layers * batch * hkv * ((cap + TILE - 1) // TILE) > 2_000_000:
+            continue
+        lens = [rng.choice([0, 1, cap, rng.randint(0, cap), cap + 9, -3]) for _ in range(batch)]
+        nt = [(min(max(l, 0), cap) + TILE - 1) // TILE for l in lens]
+        N = n_layers * hkv * sum(nt)
+        if N == 0:
+            continue
+        slots = library_slots(n_layers, batch, hkv, cap, 256)
+        grid = rng.choice([256, 512, MAX_GRID, 250, 7])
+        paired = rng.random() < 0.8
+        sp = stats_split(N, grid, paired, rng.choice(list(WEIGHTS.values())))
+        b = [sp.begin(w) for w in range(sp.G + 1)]
+        assert b[0] == 0 and b[-1] == N and all(b[w + 1] > b[w] for w in range(sp.G))
+        for c in rng.sample(range(N), min(N, 300)) + [0, N - 1]:
+            w = sp.owner(c)
+            assert b[w] <= c < b[w + 1]
+        c = 0
+        for _layer in range(n_layers):
+            for bb in range(batch):
+                for _h in range(hkv):
+                    if nt[bb]:
+                        span = sp.owner(c + nt[bb] - 1) - sp.owner(c) + 1
+                        assert span <= slots, (span, slots, n_layers, batch, hkv, cap, lens, grid)
+                        worst = max(worst, span - slots)
+                        c += nt[bb]
+        assert c == N
+    return worst
+
+
+def test_stats_split_fits_the_slots():
+    worst = max(_check_random_shapes(seed) for seed in range(6))
+    # some unit is met by exactly as many workgroups as there are slots: one slot fewer in
+    # the library's sizing would lose partials on these shapes
+    assert worst == 0
