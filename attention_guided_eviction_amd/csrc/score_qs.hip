@@ -18,6 +18,7 @@
 // with f - 1), and the loads of f + kSlots - 1 go into the slot f - 1 used.
 #include <algorithm>
 #include <mutex>
+#include <type_traits>
 
 #include "score_common.h"
 
@@ -276,12 +277,15 @@ __device__ inline void stats_loop(const uint16_t* kp, const UnitInfo& ui, int ke
                                   const RowRegs<D, BPW>& q, RowStat (&st)[BPW], float c) {
   using C = Qs<D, NW>;
   f32x16 A[BPW], B[BPW];
-  auto step = [&](int f, f32x16(&nxt)[BPW], f32x16(&cur)[BPW]) {
+  // slot_c: the ring slot of fragment f (f % kSlots) as a compile-time constant, so the slot
+  // offsets of the loads and LDS reads are immediates
+  auto step = [&](auto slot_c, int f, f32x16(&nxt)[BPW], f32x16(&cur)[BPW]) {
+    constexpr int kSlot = decltype(slot_c)::value;
     ring_wait<waitcnt_imm((kAhead - 1) * C::kPerWave, 0)>();
     const int fa = f + kAhead < nf ? f + kAhead : nf - 1;
-    issue_fragment<D, NW>(kp, key_begin + 32 * fa, ui.L, ring + ((f + kAhead) % kSlots) * C::kFragBytes);
+    issue_fragment<D, NW>(kp, key_begin + 32 * fa, ui.L, ring + ((kSlot + kAhead) % kSlots) * C::kFragBytes);
     KeyRegs<D> k;
-    read_keys<D>(ring + (f % kSlots) * C::kFragBytes, k);
+    read_keys<D>(ring + kSlot * C::kFragBytes, k);
     if (f == 0) {
       stats_first<D, BPW, NB>(k, q, nxt);
     } else {
@@ -292,9 +296,12 @@ __device__ inline void stats_loop(const uint16_t* kp, const UnitInfo& ui, int ke
         stats_step<D, BPW, NB, false>(k, q, cur, nxt, st, pkey0, ui.L, c);
     }
   };
-  for (int f = 0; f < nf; f += 2) {
-    step(f, A, B);
-    if (f + 1 < nf) step(f + 1, B, A);
+  static_assert(kSlots == 4, "the loop below walks the ring slots in order");
+  for (int f = 0; f < nf; f += 4) {
+    step(std::integral_constant<int, 0>{}, f, A, B);
+    if (f + 1 < nf) step(std::integral_constant<int, 1>{}, f + 1, B, A);
+    if (f + 2 < nf) step(std::integral_constant<int, 2>{}, f + 2, A, B);
+    if (f + 3 < nf) step(std::integral_constant<int, 3>{}, f + 3, B, A);
   }
   auto drain = [&](f32x16(&last)[BPW]) {
     const int pkey0 = key_begin + 32 * (nf - 1);
