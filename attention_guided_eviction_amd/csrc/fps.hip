@@ -11,7 +11,9 @@
 // picked row straight from its (read-only) source through scalar loads and each thread
 // takes the dot product of its row with it by v_dot2_f32_bf16 with the row in SGPRs: no
 // cross-lane reduction per row.  Each thread keeps its row's distance to the nearest
-// chosen row; a block-wide max of (distance, lowest index on ties) names the next pick.
+// chosen row; a block-wide max of (distance, lowest index on ties) names the next pick:
+// a DPP max per wave, then one 64-bit LDS atomic max per wave of (distance key, complement
+// of the index), read back by every thread after the pick's one barrier.
 #include <mutex>
 
 #include "bkv_internal.h"
@@ -45,8 +47,7 @@ template <int D>
 __global__ __launch_bounds__(kFpsThreads) void fps_kernel(const FpsArgs a) {
   constexpr int W = D / 2;   // 32-bit words (bf16 pairs) per row
   __shared__ float inv_s[kFpsThreads];
-  __shared__ unsigned best_v[2][kWaves];
-  __shared__ int best_i[2][kWaves];
+  __shared__ unsigned long long best[3];   // per pick (mod 3): max of (distance key << 32 | ~index)
   const int nthr = static_cast<int>(blockDim.x);
   const int nwaves = nthr >> 6;
 
@@ -106,6 +107,7 @@ __global__ __launch_bounds__(kFpsThreads) void fps_kernel(const FpsArgs a) {
   for (int i = 0; i < W; ++i) ss = dot2(x[i], x[i], ss);
   const float inv = 1.0f / fmaxf(sqrtf(ss), 1e-30f);
   inv_s[tid] = inv;
+  if (tid == 0) best[0] = 0ull;
   __syncthreads();   // every row's inverse norm is read by index below
 
   float mind = 0.f;
@@ -132,23 +134,17 @@ __global__ __launch_bounds__(kFpsThreads) void fps_kernel(const FpsArgs a) {
       key = avail ? __float_as_uint(mind) + 1u : 0u;
     }
     const unsigned wmax = wave_umax(key);
-    // lowest lane holding the wave max = lowest pool index of the wave
+    // lowest lane holding the wave max = lowest pool index of the wave; one LDS max per
+    // wave of (key, complement of the index): the largest key wins, then the lowest index
     const unsigned long long hit = __ballot(key == wmax);
+    if (tid == 0) best[(t + 1) % 3] = 0ull;   // last read before the previous pick's barrier
     if ((tid & 63) == 0) {
-      best_v[t & 1][tid >> 6] = wmax;
-      best_i[t & 1][tid >> 6] = (tid & ~63) + __ffsll(static_cast<long long>(hit)) - 1;
+      const unsigned idx = static_cast<unsigned>((tid & ~63) + __ffsll(static_cast<long long>(hit)) - 1);
+      atomicMax(&best[t % 3], (static_cast<unsigned long long>(wmax) << 32) | (0xffffffffu - idx));
     }
     __syncthreads();
-    unsigned bv = best_v[t & 1][0];
-    int bi = best_i[t & 1][0];
-    for (int w = 1; w < nwaves; ++w) {   // waves in index order: strict > keeps the lowest
-      const unsigned ov = best_v[t & 1][w];
-      if (ov > bv) {
-        bv = ov;
-        bi = best_i[t & 1][w];
-      }
-    }
-    cur = __builtin_amdgcn_readfirstlane(bi);
+    const unsigned long long bw = best[t % 3];
+    cur = __builtin_amdgcn_readfirstlane(static_cast<int>(0xffffffffu - static_cast<unsigned>(bw)));
   }
   if (tid == 0) a.n_out[layer][bh] = a.nb_max;
 }
