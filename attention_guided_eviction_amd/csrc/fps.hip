@@ -7,13 +7,14 @@
 // row (the workgroup is the largest pool rounded up to whole waves, so two units share a CU
 // on the largest workloads); larger pools take fps_pool_kernel below.  Thread p
 // holds pool row p (live beacons, then the group's new queries head-major in time order)
-// in registers as packed bf16 pairs, with its inverse norm.  A pick is uniform across the workgroup, so every wave reads the
-// picked row straight from its (read-only) source through scalar loads and each thread
-// takes the dot product of its row with it by v_dot2_f32_bf16 with the row in SGPRs: no
-// cross-lane reduction per row.  Each thread keeps its row's distance to the nearest
-// chosen row; a block-wide max of (distance, lowest index on ties) names the next pick:
-// a DPP max per wave, then one 64-bit LDS atomic max per wave of (distance key, complement
-// of the index), read back by every thread after the pick's one barrier.
+// in registers as packed bf16 pairs, with its inverse norm.  The pick's owner copies its
+// row into LDS; after a barrier every wave reads it there (one address: a broadcast) into
+// scalar registers, and each thread takes the dot product of its row with it by
+// v_dot2_f32_bf16 with the row in SGPRs: no cross-lane reduction per row.  Each thread
+// keeps its row's distance to the nearest chosen row; a block-wide max of (distance,
+// lowest index on ties) names the next pick: a DPP max per wave, then one 64-bit LDS atomic
+// max per wave of (distance key, complement of the index), read back by every thread after
+// a barrier.  Two barriers per pick.
 #include <mutex>
 
 #include "bkv_internal.h"
@@ -47,7 +48,8 @@ template <int D>
 __global__ __launch_bounds__(kFpsThreads) void fps_kernel(const FpsArgs a) {
   constexpr int W = D / 2;   // 32-bit words (bf16 pairs) per row
   __shared__ float inv_s[kFpsThreads];
-  __shared__ unsigned long long best[3];   // per pick (mod 3): max of (distance key << 32 | ~index)
+  __shared__ unsigned long long best[3];
+  __shared__ uint4 pick_row[W / 4];   // the pick's row, written by its owner   // per pick (mod 3): max of (distance key << 32 | ~index)
   const int nthr = static_cast<int>(blockDim.x);
   const int nwaves = nthr >> 6;
 
@@ -117,16 +119,26 @@ __global__ __launch_bounds__(kFpsThreads) void fps_kernel(const FpsArgs a) {
     if (p == cur) {   // the pick's owner writes it out and leaves the candidates
       uint4* dst = reinterpret_cast<uint4*>(out + static_cast<size_t>(t) * D);
 #pragma unroll
-      for (int i = 0; i < W / 4; ++i) dst[i] = make_uint4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
+      for (int i = 0; i < W / 4; ++i) {
+        const uint4 v = make_uint4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
+        dst[i] = v;
+        pick_row[i] = v;
+      }
       avail = false;
     }
     if (t == a.nb_max - 1) break;
+    __syncthreads();   // the pick's row is in LDS
     unsigned key = 0;   // distance bits + 1 (monotone for distances >= 0); 0: cannot be picked
     if ((tid & ~63) < P) {   // waves holding no pool row skip the products
-      const const_u32 y = (const_u32)(row_ptr(cur));   // uniform: scalar loads
       float acc[4] = {0.f, 0.f, 0.f, 0.f};   // four chains: shorter dependency
 #pragma unroll
-      for (int i = 0; i < W; ++i) acc[i & 3] = dot2(x[i], y[i], acc[i & 3]);
+      for (int i = 0; i < W / 4; ++i) {
+        const uint4 v = pick_row[i];   // one address for the wave: a broadcast
+        acc[0] = dot2(x[4 * i], __builtin_amdgcn_readfirstlane(v.x), acc[0]);
+        acc[1] = dot2(x[4 * i + 1], __builtin_amdgcn_readfirstlane(v.y), acc[1]);
+        acc[2] = dot2(x[4 * i + 2], __builtin_amdgcn_readfirstlane(v.z), acc[2]);
+        acc[3] = dot2(x[4 * i + 3], __builtin_amdgcn_readfirstlane(v.w), acc[3]);
+      }
       const float dt = (acc[0] + acc[1]) + (acc[2] + acc[3]);
       float d = 1.0f - dt * inv * inv_s[cur];
       d = fminf(fmaxf(d, 0.f), 2.f);
