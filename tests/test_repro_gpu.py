@@ -1,0 +1,78 @@
+"""Reproducibility of the library's outputs on the GPU.
+
+* The same call on the same inputs gives bit-identical outputs (every floating-point sum
+  runs in a fixed order; the only atomics are integer ones).
+* How the stats pass splits a unit's keys into partial sums follows the launch size, so
+  scoring the layers in two calls instead of one may change the last bits of the scores:
+  the two must agree to 1e-4 relative (fp32 sums of the same terms in another order), far
+  inside the 1e-3 parity tolerance against the oracle.
+"""
+import pytest
+import torch
+
+from synth import WORKLOADS
+from parity import build_inputs, event_config, log
+from attention_guided_eviction_amd import bkv
+from attention_guided_eviction_amd.event import CompressionEvent
+
+pytestmark = pytest.mark.gpu
+
+SPLIT_RTOL = 1e-4
+
+
+def _event(w):
+    inp = build_inputs(w)
+    ev = CompressionEvent(event_config(w), inp["seq_len"], "cuda")
+    ev.bind(inp["k"], inp["v"], inp["q"], inp["beacons"], inp["n_beacons"])
+    return ev, inp
+
+
+def _outputs(ev):
+    return [t.clone() for t in ev.scores + ev.idx + ev.n_kept + ev.k_out + ev.v_out]
+
+
+@pytest.mark.parametrize("name", ["qwen7b_16k", "llama8b_32k"])
+def test_repeat_call_bit_identical(name):
+    w = WORKLOADS[name].replace(name=f"repro_{name}", n_layers=3, batch=2, capacity=4000, ragged=(1800, 4000))
+    ev, _ = _event(w)
+
+    def clear():   # outputs past a sequence's length are not written: same contents both times
+        for t in ev.scores + ev.idx + ev.n_kept + ev.k_out + ev.v_out:
+            t.zero_()
+
+    clear()
+    ev.calls["compress"]()
+    torch.cuda.synchronize()
+    first = _outputs(ev)
+    clear()
+    ev.calls["compress"]()
+    torch.cuda.synchronize()
+    for a, b in zip(first, _outputs(ev)):
+        assert torch.equal(a, b)
+    log(f"[repro] {name}: repeated event bit-identical")
+
+
+def test_layer_split_scores_agree():
+    """Scores from one call over 4 layers against two calls over 2 layers each (G = 4, five
+    row blocks: the shape where the partition of the keys differs most)."""
+    w = WORKLOADS["llama8b_32k"].replace(name="repro_split", n_layers=4, batch=2, capacity=5000,
+                                         ragged=(2100, 5000))
+    ev, inp = _event(w)
+    ev.calls["score"]()
+    torch.cuda.synchronize()
+    whole = [t.clone() for t in ev.scores]
+    parts = [torch.empty_like(t) for t in ev.scores]
+    for a, b in ((0, 2), (2, 4)):
+        sh = bkv.CacheShape(b - a, w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.capacity, inp["seq_len"])
+        bkv.score(sh, inp["k"][a:b], inp["q"][a:b], w.q_len, w.window, inp["beacons"][a:b], inp["n_beacons"][a:b],
+                  w.nb_max, parts[a:b], ev.workspace)
+    torch.cuda.synchronize()
+    lens = inp["seq_len"].cpu().tolist()
+    worst = 0.0
+    for l in range(w.n_layers):
+        for b_, L in enumerate(lens):
+            x, y = whole[l][b_, :, :L].double(), parts[l][b_, :, :L].double()
+            rel = ((x - y).abs() / x.abs().clamp_min(1e-300)).max().item()
+            worst = max(worst, rel)
+            assert rel <= SPLIT_RTOL, f"layer {l} sequence {b_}: relative difference {rel:.2e}"
+    log(f"[repro] layer split: worst relative score difference {worst:.2e}")
