@@ -6,12 +6,33 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "bkv.h"
 
 namespace bkv {
 
 // One launch covers up to this many layers; the host splits longer models.
 constexpr int kMaxLayers = 48;
+
+// Kernel attributes (the dynamic LDS limit) belong to a device: `set` runs once for each
+// device it is called on (the current one) and its result is returned on every later call
+// there.  Devices past kMaxDevices are refused.
+constexpr int kMaxDevices = 64;
+struct PerDeviceOnce {
+  std::once_flag flag[kMaxDevices];
+  hipError_t err[kMaxDevices] = {};
+};
+
+template <class F>
+hipError_t once_per_device(PerDeviceOnce& o, F set) {
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(o.flag[dev], [&] { o.err[dev] = set(); });
+  return o.err[dev];
+}
 
 // ---- score ----------------------------------------------------------------------------------
 // Two persistent kernels (see score.hip).  A tile is kScoreTile keys of one unit; the grid is

@@ -15,7 +15,6 @@
 // lowest index on ties) names the next pick: a DPP max per wave, then one 64-bit LDS atomic
 // max per wave of (distance key, complement of the index), read back by every thread after
 // a barrier.  Two barriers per pick.
-#include <mutex>
 
 #include "bkv_internal.h"
 
@@ -48,10 +47,9 @@ template <int D>
 __global__ __launch_bounds__(kFpsThreads) void fps_kernel(const FpsArgs a) {
   constexpr int W = D / 2;   // 32-bit words (bf16 pairs) per row
   __shared__ float inv_s[kFpsThreads];
-  __shared__ unsigned long long best[3];
-  __shared__ uint4 pick_row[W / 4];   // the pick's row, written by its owner   // per pick (mod 3): max of (distance key << 32 | ~index)
+  __shared__ unsigned long long best[3];   // per pick (mod 3): max of (distance key << 32 | ~index)
+  __shared__ uint4 pick_row[W / 4];        // the pick's row, written by its owner
   const int nthr = static_cast<int>(blockDim.x);
-  const int nwaves = nthr >> 6;
 
   const int u = blockIdx.x;
   const int per_layer = a.batch * a.n_kv_heads;
@@ -337,15 +335,15 @@ hipError_t launch_fps(const FpsArgs& a, int n_layers, int head_dim, int pool_max
   if (pool_max > kFpsThreads * kFpsPoolRowsPerThread) return hipErrorInvalidValue;   // rejected by the host beforehand
   const unsigned grid = static_cast<unsigned>(n_layers) * a.batch * a.n_kv_heads;
   if (pool_max > kFpsRegisterPool) {
-    static std::once_flag once;
-    static hipError_t attr_err = hipSuccess;
-    std::call_once(once, [] {
+    static PerDeviceOnce once;
+    const hipError_t attr_err = once_per_device(once, [] {
       const int lds = kFpsThreads * kFpsPoolRowsPerThread * static_cast<int>(sizeof(float2));
-      attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&fps_pool_kernel<128>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-      if (attr_err == hipSuccess)
-        attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&fps_pool_kernel<64>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fps_pool_kernel<128>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+      if (e == hipSuccess)
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fps_pool_kernel<64>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+      return e;
     });
     if (attr_err != hipSuccess) return note_hip_error(attr_err, "fps: hipFuncSetAttribute");
     const size_t lds = static_cast<size_t>(pool_max) * sizeof(float2);

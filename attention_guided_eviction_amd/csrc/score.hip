@@ -32,7 +32,6 @@
 // over rows reduces inside the lane.  Blocks of 32 rows run two at a time in ping-pong
 // accumulators: the products of one block are issued among the vector work of the other.
 #include <algorithm>
-#include <mutex>
 
 #include "score_common.h"
 
@@ -665,23 +664,18 @@ size_t lds_bytes(int head_dim, int obs_pad) {
 
 template <int D>
 hipError_t launch_d(ScoreArgs a, int n_layers, hipStream_t s) {
-  static std::once_flag once;
-  static hipError_t attr_err = hipSuccess;
-  std::call_once(once, [] {
-    attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&score_kernel<D, false>),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (attr_err == hipSuccess)
-      attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&score_kernel<D, true>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (attr_err == hipSuccess)
-      attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&score_kernel<D, true, true>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (attr_err == hipSuccess)
-      attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&finish8_kernel<D, true>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (attr_err == hipSuccess)
-      attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&finish8_kernel<D, false>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  static PerDeviceOnce once;
+  const hipError_t attr_err = once_per_device(once, [] {
+    const void* kernels[] = {reinterpret_cast<const void*>(&score_kernel<D, false>),
+                             reinterpret_cast<const void*>(&score_kernel<D, true>),
+                             reinterpret_cast<const void*>(&score_kernel<D, true, true>),
+                             reinterpret_cast<const void*>(&finish8_kernel<D, true>),
+                             reinterpret_cast<const void*>(&finish8_kernel<D, false>)};
+    for (const void* k : kernels) {
+      const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
   });
   if (attr_err != hipSuccess) return note_hip_error(attr_err, "score: hipFuncSetAttribute");
   const size_t lds = lds_bytes(D, a.obs_pad);

@@ -17,7 +17,6 @@
 // vmcnt), the workgroup meets at a barrier (now all of f is in LDS and every wave is done
 // with f - 1), and the loads of f + kSlots - 1 go into the slot f - 1 used.
 #include <algorithm>
-#include <mutex>
 #include <type_traits>
 
 #include "score_common.h"
@@ -447,13 +446,11 @@ constexpr int threads_of() {
 
 template <int D, int BPW>
 hipError_t prepare() {
-  static std::once_flag once;
-  static hipError_t err = hipSuccess;
-  std::call_once(once, [] {
-    err = hipFuncSetAttribute(reinterpret_cast<const void*>(qs_kernel_of<D, BPW>()),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(qs_lds_bytes<D>()));
+  static PerDeviceOnce once;
+  return once_per_device(once, [] {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(qs_kernel_of<D, BPW>()),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(qs_lds_bytes<D>()));
   });
-  return err;
 }
 
 template <int D, int BPW>
