@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <vector>
 
 #include "bkv_internal.h"
 
@@ -44,10 +45,44 @@ bool all_set(T const* arr, int n) {
   return true;
 }
 
-bool overlap(const void* a, size_t na, const void* b, size_t nb) {
-  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
-  return na > 0 && nb > 0 && x < y + nb && y < x + na;
-}
+// The device memory one call reads and writes.  No output may overlap anything else the
+// call touches: an input of any layer, the workspace or another output; inputs may share
+// memory.  clash() sorts the regions by address and sweeps them once.
+class Footprint {
+ public:
+  void in(const void* p, size_t n) { add(p, n, false); }
+  void out(const void* p, size_t n) { add(p, n, true); }
+  template <typename T>
+  void in_layers(T const* arr, int n_layers, size_t bytes) {
+    for (int l = 0; l < n_layers; ++l) in(arr[l], bytes);
+  }
+  template <typename T>
+  void out_layers(T const* arr, int n_layers, size_t bytes) {
+    for (int l = 0; l < n_layers; ++l) out(arr[l], bytes);
+  }
+  bool clash() {
+    std::sort(r_.begin(), r_.end(), [](const R& x, const R& y) { return x.b < y.b; });
+    uintptr_t end_any = 0, end_out = 0;   // furthest end of the regions before, of the outputs before
+    for (const R& x : r_) {
+      if (x.b < (x.out ? end_any : end_out)) return true;
+      end_any = std::max(end_any, x.e);
+      if (x.out) end_out = std::max(end_out, x.e);
+    }
+    return false;
+  }
+
+ private:
+  struct R {
+    uintptr_t b, e;
+    bool out;
+  };
+  void add(const void* p, size_t n, bool is_out) {
+    if (p == nullptr || n == 0) return;
+    const uintptr_t b = reinterpret_cast<uintptr_t>(p);
+    r_.push_back(R{b, n > UINTPTR_MAX - b ? UINTPTR_MAX : b + n, is_out});
+  }
+  std::vector<R> r_;
+};
 
 // Bytes of one layer of a [batch][heads][rows][cols] array of `elem`-byte items.
 size_t layer_bytes(const bkv_shape* s, int heads, long long rows, long long cols, size_t elem) {
@@ -101,10 +136,25 @@ bkv_status check_score_args(const bkv_shape* s, const void* const* k, const void
   if (static_cast<long long>(g) * window + nb_max > BKV_MAX_OBS) return BKV_EUNSUPPORTED;
   const size_t kb = layer_bytes(s, s->n_kv_heads, s->capacity, s->head_dim, 2);
   const size_t sb = layer_bytes(s, s->n_kv_heads, s->capacity, 1, 4);
-  if (kb == SIZE_MAX || sb == SIZE_MAX) return BKV_EINVAL;
-  for (int l = 0; l < s->n_layers; ++l)
-    if (overlap(scores[l], sb, k[l], kb)) return BKV_EALIAS;
+  const size_t qb = layer_bytes(s, s->n_q_heads, q_len, s->head_dim, 2);
+  const size_t bb = layer_bytes(s, s->n_kv_heads, nb_max, s->head_dim, 2);
+  if (kb == SIZE_MAX || sb == SIZE_MAX || qb == SIZE_MAX || bb == SIZE_MAX) return BKV_EINVAL;
   return BKV_OK;
+}
+
+size_t seq_len_bytes(const bkv_shape* s) { return static_cast<size_t>(s->batch) * sizeof(int32_t); }
+
+// What scoring reads: K, the stored queries (window > 0), the beacons and their counts
+// (nb_max > 0), the lengths.  Sizes were checked by check_score_args.
+void score_inputs(Footprint& f, const bkv_shape* s, const void* const* k, const void* const* q, int32_t q_len,
+                  int32_t window, const void* const* beacons, const int32_t* const* n_beacons, int32_t nb_max) {
+  f.in_layers(k, s->n_layers, layer_bytes(s, s->n_kv_heads, s->capacity, s->head_dim, 2));
+  if (window > 0) f.in_layers(q, s->n_layers, layer_bytes(s, s->n_q_heads, q_len, s->head_dim, 2));
+  if (nb_max > 0) {
+    f.in_layers(beacons, s->n_layers, layer_bytes(s, s->n_kv_heads, nb_max, s->head_dim, 2));
+    f.in_layers(n_beacons, s->n_layers, layer_bytes(s, s->n_kv_heads, 1, 1, 4));
+  }
+  f.in(s->seq_len, seq_len_bytes(s));
 }
 
 bkv_status check_select_args(const bkv_shape* s, const float* const* scores, int32_t budget, int32_t window,
@@ -119,11 +169,12 @@ bkv_status check_select_args(const bkv_shape* s, const float* const* scores, int
   const size_t ib = layer_bytes(s, s->n_kv_heads, budget, 1, 4);
   const size_t nb = layer_bytes(s, s->n_kv_heads, 1, 1, 4);
   if (sb == SIZE_MAX || ib == SIZE_MAX) return BKV_EINVAL;
-  for (int l = 0; l < s->n_layers; ++l)
-    if (overlap(idx[l], ib, scores[l], sb) || overlap(n_kept[l], nb, scores[l], sb) ||
-        overlap(n_kept[l], nb, idx[l], ib))
-      return BKV_EALIAS;
-  return BKV_OK;
+  Footprint f;
+  f.in_layers(scores, s->n_layers, sb);
+  f.in(s->seq_len, seq_len_bytes(s));
+  f.out_layers(idx, s->n_layers, ib);
+  f.out_layers(n_kept, s->n_layers, nb);
+  return f.clash() ? BKV_EALIAS : BKV_OK;
 }
 
 bkv_status check_compact_args(const bkv_shape* s, const void* const* k, const void* const* v,
@@ -137,13 +188,16 @@ bkv_status check_compact_args(const bkv_shape* s, const void* const* k, const vo
     return BKV_EINVAL;
   const size_t kb = layer_bytes(s, s->n_kv_heads, s->capacity, s->head_dim, 2);
   const size_t ob = layer_bytes(s, s->n_kv_heads, out_capacity, s->head_dim, 2);
-  if (kb == SIZE_MAX || ob == SIZE_MAX) return BKV_EINVAL;
-  for (int l = 0; l < s->n_layers; ++l) {
-    if (overlap(k_out[l], ob, k[l], kb) || overlap(k_out[l], ob, v[l], kb) || overlap(v_out[l], ob, k[l], kb) ||
-        overlap(v_out[l], ob, v[l], kb) || overlap(k_out[l], ob, v_out[l], ob))
-      return BKV_EALIAS;
-  }
-  return BKV_OK;
+  const size_t ib = layer_bytes(s, s->n_kv_heads, budget, 1, 4);
+  if (kb == SIZE_MAX || ob == SIZE_MAX || ib == SIZE_MAX) return BKV_EINVAL;
+  Footprint f;
+  f.in_layers(k, s->n_layers, kb);
+  f.in_layers(v, s->n_layers, kb);
+  f.in_layers(idx, s->n_layers, ib);
+  f.in_layers(n_kept, s->n_layers, layer_bytes(s, s->n_kv_heads, 1, 1, 4));
+  f.out_layers(k_out, s->n_layers, ob);
+  f.out_layers(v_out, s->n_layers, ob);
+  return f.clash() ? BKV_EALIAS : BKV_OK;
 }
 
 bkv_status hip_status(hipError_t e) { return e == hipSuccess ? BKV_OK : BKV_EHIP; }
@@ -220,6 +274,11 @@ bkv_status bkv_score_agg(const bkv_shape* shape, const void* const* k, const voi
   if (workspace == nullptr || workspace_bytes < ws.total ||
       reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
     return BKV_EWORKSPACE;
+  Footprint f;
+  score_inputs(f, shape, k, q, q_len, window, beacons, n_beacons, nb_max);
+  f.out_layers(scores, shape->n_layers, layer_bytes(shape, shape->n_kv_heads, shape->capacity, 1, 4));
+  f.out(workspace, ws.total);
+  if (f.clash()) return BKV_EALIAS;
   ScoreArgs a;
   memset(&a, 0, sizeof(a));
   a.seq_len = shape->seq_len;
@@ -346,11 +405,13 @@ bkv_status bkv_update_beacons_policy(const bkv_shape* shape, const void* const* 
   const size_t qb = layer_bytes(shape, shape->n_q_heads, q_len, shape->head_dim, 2);
   const size_t cb = layer_bytes(shape, shape->n_kv_heads, 1, 1, 4);
   if (bb == SIZE_MAX || qb == SIZE_MAX) return BKV_EINVAL;
-  for (int l = 0; l < shape->n_layers; ++l) {
-    if (overlap(beacons_out[l], bb, beacons_in[l], bb) || overlap(n_out[l], cb, n_in[l], cb) ||
-        (t_new > 0 && overlap(beacons_out[l], bb, q_new[l], qb)))
-      return BKV_EALIAS;
-  }
+  Footprint f;
+  f.in_layers(beacons_in, shape->n_layers, bb);
+  f.in_layers(n_in, shape->n_layers, cb);
+  if (t_new > 0) f.in_layers(q_new, shape->n_layers, qb);
+  f.out_layers(beacons_out, shape->n_layers, bb);
+  f.out_layers(n_out, shape->n_layers, cb);
+  if (f.clash()) return BKV_EALIAS;
   FpsArgs a;
   memset(&a, 0, sizeof(a));
   a.batch = shape->batch;
@@ -390,6 +451,18 @@ bkv_status bkv_compress(const bkv_shape* shape, const void* const* k, const void
   if (st == BKV_OK) st = check_select_args(shape, scores, budget, window, idx, n_kept);
   if (st == BKV_OK) st = check_compact_args(shape, k, v, idx, n_kept, budget, budget, k_out, v_out);
   if (st != BKV_OK) return st;
+  // the three stages' outputs must not overlap each other either (scores, idx and n_kept
+  // are read by the later stages)
+  Footprint f;
+  score_inputs(f, shape, k, q, q_len, window, beacons, n_beacons, nb_max);
+  f.in_layers(v, shape->n_layers, layer_bytes(shape, shape->n_kv_heads, shape->capacity, shape->head_dim, 2));
+  f.out_layers(scores, shape->n_layers, layer_bytes(shape, shape->n_kv_heads, shape->capacity, 1, 4));
+  f.out_layers(idx, shape->n_layers, layer_bytes(shape, shape->n_kv_heads, budget, 1, 4));
+  f.out_layers(n_kept, shape->n_layers, layer_bytes(shape, shape->n_kv_heads, 1, 1, 4));
+  f.out_layers(k_out, shape->n_layers, layer_bytes(shape, shape->n_kv_heads, budget, shape->head_dim, 2));
+  f.out_layers(v_out, shape->n_layers, layer_bytes(shape, shape->n_kv_heads, budget, shape->head_dim, 2));
+  if (workspace != nullptr) f.out(workspace, std::min(workspace_bytes, score_ws(shape, window, nb_max).total));
+  if (f.clash()) return BKV_EALIAS;
   st = bkv_score(shape, k, q, q_len, window, beacons, n_beacons, nb_max, scores, workspace, workspace_bytes, stream);
   if (st != BKV_OK) return st;
   st = bkv_select_topk(shape, scores, budget, window, idx, n_kept, nullptr, 0, stream);
@@ -419,11 +492,14 @@ bkv_status bkv_decode_attention(const bkv_shape* shape, const void* const* q, co
   const size_t ob = layer_bytes(shape, shape->n_q_heads, 1, shape->head_dim, 4);
   const size_t kb = layer_bytes(shape, shape->n_kv_heads, shape->capacity, shape->head_dim, 2);
   if (qb == SIZE_MAX || ob == SIZE_MAX || kb == SIZE_MAX) return BKV_EINVAL;
-  for (int l = 0; l < shape->n_layers; ++l) {
-    if (overlap(out[l], ob, q[l], qb) || overlap(out[l], ob, k[l], kb) || overlap(out[l], ob, v[l], kb) ||
-        overlap(out[l], ob, workspace, ws.total))
-      return BKV_EALIAS;
-  }
+  Footprint f;
+  f.in_layers(q, shape->n_layers, qb);
+  f.in_layers(k, shape->n_layers, kb);
+  f.in_layers(v, shape->n_layers, kb);
+  f.in(shape->seq_len, seq_len_bytes(shape));
+  f.out_layers(out, shape->n_layers, ob);
+  f.out(workspace, ws.total);
+  if (f.clash()) return BKV_EALIAS;
   DecodeArgs a;
   memset(&a, 0, sizeof(a));
   char* wsp = static_cast<char*>(workspace);

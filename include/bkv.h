@@ -47,6 +47,11 @@
  * stream order; results are visible after the caller synchronises.  Calls are
  * thread-safe; concurrent calls must not share output or workspace buffers.
  *
+ * Overlap.  No output of a call (nor its workspace) may overlap anything else the call
+ * touches: an input of any layer, seq_len, the workspace or another output, counted as
+ * whole per-layer arrays of the layouts above.  Inputs may share memory.  A call that
+ * breaks this returns BKV_EALIAS.
+ *
  * Errors.  Arguments are checked on the host before anything is enqueued; a failing call
  * enqueues nothing and returns a negative bkv_status.  Device-resident values are not
  * errors: seq_len[b] is clamped to [0, capacity] and beacon counts to [0, nb_max] inside
@@ -70,7 +75,7 @@ typedef enum bkv_status {
   BKV_EINVAL = -1,        /* null pointer, non-positive size, window > budget, ...     */
   BKV_EUNSUPPORTED = -2,  /* valid but outside what the kernels support (head_dim,      */
                           /* observation rows, beacon pool size)                        */
-  BKV_EALIAS = -3,        /* an output overlaps an input it must not overlap            */
+  BKV_EALIAS = -3,        /* an output overlaps an input, the workspace or an output    */
   BKV_EWORKSPACE = -4,    /* workspace missing or smaller than the *_workspace_bytes    */
   BKV_EHIP = -5           /* a HIP launch or runtime call failed                        */
 } bkv_status;
@@ -123,8 +128,8 @@ const char* bkv_last_error(void);
  * q_new:   per layer bf16 [batch][n_q_heads][q_len][head_dim]; 0 <= t_new <= q_len.
  * n_in:    per layer int32 [batch][n_kv_heads].
  * Errors:  BKV_EINVAL for null arrays/pointers or bad sizes; BKV_EUNSUPPORTED if
- *          nb_max + G * t_new > BKV_MAX_POOL or head_dim is not 64/128; BKV_EALIAS if a
- *          beacons_out layer overlaps the same layer's beacons_in or q_new.
+ *          nb_max + G * t_new > BKV_MAX_POOL or head_dim is not 64/128; BKV_EALIAS if
+ *          beacons_out or n_out overlaps an input (beacons_in, n_in, q_new) or each other.
  * ---------------------------------------------------------------------------------- */
 bkv_status bkv_update_beacons(const bkv_shape* shape,
                               const void* const* beacons_in, const int32_t* const* n_in,
@@ -179,7 +184,8 @@ bkv_status bkv_update_beacons_policy(const bkv_shape* shape,
  * workspace:   device scratch of at least bkv_score_workspace_bytes(...) bytes (256-byte
  *              aligned), contents irrelevant on entry and undefined on exit.
  * Errors:      BKV_EINVAL, BKV_EUNSUPPORTED (head_dim, observation rows), BKV_EWORKSPACE,
- *              BKV_EALIAS if a scores layer overlaps that layer's K.
+ *              BKV_EALIAS if scores or the workspace overlaps an input (K, queries, beacons,
+ *              beacon counts, seq_len), each other or another scores layer.
  * ---------------------------------------------------------------------------------- */
 size_t bkv_score_workspace_bytes(const bkv_shape* shape, int32_t window, int32_t nb_max);
 
@@ -232,7 +238,8 @@ bkv_status bkv_score_agg(const bkv_shape* shape,
  *
  * 1 <= budget, 0 <= window <= budget.  workspace may be NULL when
  * bkv_select_workspace_bytes(...) returns 0.
- * Errors: BKV_EINVAL, BKV_EWORKSPACE, BKV_EALIAS if idx overlaps scores.
+ * Errors: BKV_EINVAL, BKV_EWORKSPACE, BKV_EALIAS if idx or n_kept overlaps scores,
+ *         seq_len or each other.
  * ---------------------------------------------------------------------------------- */
 size_t bkv_select_workspace_bytes(const bkv_shape* shape, int32_t budget);
 
@@ -251,7 +258,8 @@ bkv_status bkv_select_topk(const bkv_shape* shape,
  * as bit copies; rows from n up are left untouched.  Positions outside [0, capacity) are
  * clamped into it (bkv_select_topk never produces them).  Out of place: outputs must not
  * overlap K or V.
- * Errors: BKV_EINVAL, BKV_EUNSUPPORTED (head_dim), BKV_EALIAS.
+ * Errors: BKV_EINVAL, BKV_EUNSUPPORTED (head_dim), BKV_EALIAS if k_out or v_out overlaps
+ *         K, V, idx, n_kept or each other.
  * ---------------------------------------------------------------------------------- */
 bkv_status bkv_compact(const bkv_shape* shape,
                        const void* const* k, const void* const* v,
@@ -281,7 +289,8 @@ bkv_status bkv_compact_into(const bkv_shape* shape,
 /* ------------------------------------------------------------------------------------
  * One compression event: bkv_score, then bkv_select_topk, then bkv_compact, with the
  * arguments of those three calls (same meaning, same errors).  Writes scores, idx,
- * n_kept, k_out and v_out exactly as the three calls would.
+ * n_kept, k_out and v_out exactly as the three calls would.  The stages' outputs and the
+ * workspace must not overlap each other either (BKV_EALIAS), since later stages read them.
  * workspace: at least bkv_compress_workspace_bytes(...) bytes.
  * ---------------------------------------------------------------------------------- */
 size_t bkv_compress_workspace_bytes(const bkv_shape* shape, int32_t window, int32_t nb_max,
@@ -312,7 +321,8 @@ bkv_status bkv_compress(const bkv_shape* shape,
  * out:  per layer fp32 [batch][n_q_heads][head_dim].
  * workspace: at least bkv_decode_workspace_bytes(shape) bytes, 256-byte aligned.
  * Errors: BKV_EINVAL, BKV_EUNSUPPORTED (head_dim; more than 8 query heads per KV head),
- *         BKV_EWORKSPACE, BKV_EALIAS if an out layer overlaps q, k, v or the workspace.
+ *         BKV_EWORKSPACE, BKV_EALIAS if out or the workspace overlaps q, k, v, seq_len or
+ *         each other.
  * ---------------------------------------------------------------------------------- */
 size_t bkv_decode_workspace_bytes(const bkv_shape* shape);
 

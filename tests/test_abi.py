@@ -227,3 +227,44 @@ def test_decode_attention_validation():
     assert call(nbytes=need - 1) == bkv.BKV_EWORKSPACE
     assert call(ws=ws + 8) == bkv.BKV_EWORKSPACE
     assert call(out=arr(FAKE + (2 << 36) + 512)) == bkv.BKV_EALIAS                # out inside K
+
+
+def two(a, b):
+    return (ctypes.c_void_p * 2)(a, b)
+
+
+def test_outputs_may_not_overlap_anything_the_call_touches():
+    """An output may overlap no input of any layer (nor the lengths), no workspace and no
+    other output; every call below is refused before anything is enqueued."""
+    lib = bkv.load()
+    s = shape()
+    # scoring
+    assert score_call(sc=arr(FAKE + (1 << 40) + 4096)) == bkv.BKV_EALIAS                 # inside the workspace
+    assert score_call(sc=two(FAKE + (2 << 36) + (1 << 32) + 64, FAKE + (5 << 36))) == bkv.BKV_EALIAS   # layer 1's q
+    assert score_call(sc=arr(FAKE - 4)) == bkv.BKV_EALIAS                                # the lengths
+    assert score_call(sc=arr(FAKE + (5 << 36), stride=4096)) == bkv.BKV_EALIAS           # the two layers' scores
+    assert score_call(sc=arr(FAKE + (4 << 36) + 8)) == bkv.BKV_EALIAS                    # beacon counts
+    assert score_call(ws=FAKE + (1 << 36)) == bkv.BKV_EALIAS                             # workspace over K
+    # selection
+    sc = arr(FAKE + (1 << 36))
+    assert lib.bkv_select_topk(ctypes.byref(s), sc, 64, 8, arr(FAKE - 8), arr(FAKE + (3 << 36)), None, 0,
+                               None) == bkv.BKV_EALIAS                                     # idx over the lengths
+    assert lib.bkv_select_topk(ctypes.byref(s), sc, 64, 8, arr(FAKE + (2 << 36)),
+                               two(FAKE + (2 << 36) + (1 << 32) + 4, FAKE + (3 << 36)), None, 0,
+                               None) == bkv.BKV_EALIAS                                     # n_kept in idx of layer 1
+    # one event: the stages' outputs must not meet either
+    assert lib.bkv_compress(ctypes.byref(s), arr(FAKE + (1 << 36)), arr(FAKE + (6 << 36)), arr(FAKE + (2 << 36)), 32,
+                            32, arr(FAKE + (3 << 36)), arr(FAKE + (4 << 36)), 16, 64, arr(FAKE + (5 << 36)),
+                            arr(FAKE + (7 << 36)), arr(FAKE + (8 << 36)), arr(FAKE + (5 << 36) + 64),
+                            arr(FAKE + (10 << 36)), FAKE + (1 << 40), 1 << 40, None) == bkv.BKV_EALIAS   # k_out in scores
+    # beacon update
+    assert lib.bkv_update_beacons(ctypes.byref(s), arr(FAKE), arr(FAKE + (1 << 36)), 16, arr(FAKE + (2 << 36)), 128,
+                                  128, two(FAKE + (1 << 36) + (1 << 32), FAKE + (3 << 36)), arr(FAKE + (4 << 36)),
+                                  None) == bkv.BKV_EALIAS                                  # beacons_out on n_in[1]
+    # decode
+    qs, ks, vs = arr(FAKE + (1 << 36)), arr(FAKE + (2 << 36)), arr(FAKE + (3 << 36))
+    need = lib.bkv_decode_workspace_bytes(ctypes.byref(s))
+    assert lib.bkv_decode_attention(ctypes.byref(s), qs, ks, vs, arr(FAKE - 4), FAKE + (1 << 40), need,
+                                    None) == bkv.BKV_EALIAS                                # out over the lengths
+    assert lib.bkv_decode_attention(ctypes.byref(s), qs, ks, vs, arr(FAKE + (4 << 36)), FAKE + (1 << 36), need,
+                                    None) == bkv.BKV_EALIAS                                # workspace over q
