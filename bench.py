@@ -387,6 +387,9 @@ def main():
         "hbm_alg_gbs": round(total_bytes / (ms * 1e-3) / 1e9, 1),
         "hbm_alg_frac_of_peak": round(total_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "per_call_ms": {n: round(t, 4) for n, t in per.items()},
+        # every stage against HBM: its algorithmic bytes (alg_bytes) over its live duration
+        "per_call_gbs": {n: {"alg_bytes": ab[n], "achieved": round(ab[n] / (t * 1e-3) / 1e9, 1),
+                             "frac": round(ab[n] / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)} for n, t in per.items()},
         "roofline": roof,
     }
     # Same-run ceiling: a plain read+write device copy of 4 GiB moved.
