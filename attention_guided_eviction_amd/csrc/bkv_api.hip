@@ -183,6 +183,8 @@ bkv_status check_compact_args(const bkv_shape* s, const void* const* k, const vo
   bkv_status st = check_shape(s);
   if (st != BKV_OK) return st;
   if (budget < 1 || out_capacity < budget) return BKV_EINVAL;
+  // the kernel numbers a unit's 16-byte row pieces (budget * head_dim / 8) with 32-bit ints
+  if (static_cast<long long>(budget) * (s->head_dim / 8) >= (1LL << 30)) return BKV_EUNSUPPORTED;
   if (!all_set(k, s->n_layers) || !all_set(v, s->n_layers) || !all_set(idx, s->n_layers) ||
       !all_set(n_kept, s->n_layers) || !all_set(k_out, s->n_layers) || !all_set(v_out, s->n_layers))
     return BKV_EINVAL;

@@ -258,8 +258,8 @@ bkv_status bkv_select_topk(const bkv_shape* shape,
  * as bit copies; rows from n up are left untouched.  Positions outside [0, capacity) are
  * clamped into it (bkv_select_topk never produces them).  Out of place: outputs must not
  * overlap K or V.
- * Errors: BKV_EINVAL, BKV_EUNSUPPORTED (head_dim), BKV_EALIAS if k_out or v_out overlaps
- *         K, V, idx, n_kept or each other.
+ * Errors: BKV_EINVAL, BKV_EUNSUPPORTED (head_dim; budget * head_dim / 8 >= 2^30),
+ *         BKV_EALIAS if k_out or v_out overlaps K, V, idx, n_kept or each other.
  * ---------------------------------------------------------------------------------- */
 bkv_status bkv_compact(const bkv_shape* shape,
                        const void* const* k, const void* const* v,

@@ -133,6 +133,8 @@ def test_compact_rejects_aliasing():
     assert lib.bkv_compact(ctypes.byref(s), k, v, idx, nk, 64, ko, arr(FAKE + (1 << 36)), None) == bkv.BKV_EALIAS
     assert lib.bkv_compact(ctypes.byref(s), k, v, idx, nk, 64, ko, ko, None) == bkv.BKV_EALIAS
     assert lib.bkv_compact(ctypes.byref(s), k, nulls(), idx, nk, 64, ko, vo, None) == bkv.BKV_EINVAL
+    # 2^27 kept rows of 16 pieces each: past what the kernel's 32-bit piece index covers
+    assert lib.bkv_compact(ctypes.byref(s), k, v, idx, nk, 1 << 27, ko, vo, None) == bkv.BKV_EUNSUPPORTED
 
 
 def test_update_beacons_rejects():
