@@ -24,7 +24,9 @@ from typing import List, Optional, Sequence
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libbkv.so")
+# BKV_LIBRARY names another build of the same library (e.g. the host-only sanitized build
+# that the ABI tests load); by default the in-tree libbkv.so.
+LIB_PATH = os.environ.get("BKV_LIBRARY") or os.path.join(_HERE, "libbkv.so")
 
 BKV_OK, BKV_EINVAL, BKV_EUNSUPPORTED, BKV_EALIAS, BKV_EWORKSPACE, BKV_EHIP = 0, -1, -2, -3, -4, -5
 MAX_OBS = 512

@@ -1,7 +1,7 @@
 """Beacon coverage of future queries: how close the kept query set stays to the queries
-decoding will issue later (BeaconKV page, Figure 6 (a): maximum cosine similarity to
-future decoding-step queries under different past-query selections; Figure 7: continual
-versus naive FPS; Table 3: Initial+Recent).
+decoding will issue later (BeaconKV page, Figure 6 (a): how similar later queries are to
+the best match in each choice of kept past queries; Figure 7: continual versus naive FPS;
+Table 3: Initial+Recent).
 
 The beacon sets are built on the GPU by the library's beacon update, chunk after chunk of a
 query stream; the similarity readout is a small evaluation, not part of the compression

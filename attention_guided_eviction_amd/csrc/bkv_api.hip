@@ -27,12 +27,17 @@ bool mul_ok(size_t a, size_t b, size_t* out) {
   return true;
 }
 
+// The kernels move bf16 rows (K, V, queries, beacons, compacted caches) in 16-byte pieces
+// and fp32 / int32 arrays element by element: every layer pointer must be aligned to that.
+constexpr uintptr_t kRowAlign = 16, kElemAlign = 4;
+
 bkv_status check_shape(const bkv_shape* s) {
   if (s == nullptr || s->seq_len == nullptr) return BKV_EINVAL;
   if (s->n_layers < 1 || s->batch < 1 || s->n_q_heads < 1 || s->n_kv_heads < 1 || s->capacity < 1 ||
       s->head_dim < 1)
     return BKV_EINVAL;
   if (s->n_q_heads % s->n_kv_heads != 0) return BKV_EINVAL;
+  if (reinterpret_cast<uintptr_t>(s->seq_len) % kElemAlign != 0) return BKV_EINVAL;
   if (s->head_dim != 64 && s->head_dim != 128) return BKV_EUNSUPPORTED;
   return BKV_OK;
 }
@@ -42,6 +47,13 @@ bool all_set(T const* arr, int n) {
   if (arr == nullptr) return false;
   for (int i = 0; i < n; ++i)
     if (arr[i] == nullptr) return false;
+  return true;
+}
+
+template <typename T>
+bool all_aligned(T const* arr, int n, uintptr_t align) {
+  for (int i = 0; i < n; ++i)
+    if (reinterpret_cast<uintptr_t>(arr[i]) % align != 0) return false;
   return true;
 }
 
@@ -132,6 +144,10 @@ bkv_status check_score_args(const bkv_shape* s, const void* const* k, const void
   if (!all_set(k, s->n_layers) || !all_set(scores, s->n_layers)) return BKV_EINVAL;
   if (window > 0 && !all_set(q, s->n_layers)) return BKV_EINVAL;
   if (nb_max > 0 && (!all_set(beacons, s->n_layers) || !all_set(n_beacons, s->n_layers))) return BKV_EINVAL;
+  if (!all_aligned(k, s->n_layers, kRowAlign) || !all_aligned(scores, s->n_layers, kElemAlign) ||
+      (window > 0 && !all_aligned(q, s->n_layers, kRowAlign)) ||
+      (nb_max > 0 && (!all_aligned(beacons, s->n_layers, kRowAlign) || !all_aligned(n_beacons, s->n_layers, kElemAlign))))
+    return BKV_EINVAL;
   const int g = s->n_q_heads / s->n_kv_heads;
   if (static_cast<long long>(g) * window + nb_max > BKV_MAX_OBS) return BKV_EUNSUPPORTED;
   const size_t kb = layer_bytes(s, s->n_kv_heads, s->capacity, s->head_dim, 2);
@@ -164,6 +180,9 @@ bkv_status check_select_args(const bkv_shape* s, const float* const* scores, int
   if (budget < 1 || window < 0 || window > budget) return BKV_EINVAL;
   if (!all_set(scores, s->n_layers) || !all_set(idx, s->n_layers) || !all_set(n_kept, s->n_layers))
     return BKV_EINVAL;
+  if (!all_aligned(scores, s->n_layers, kElemAlign) || !all_aligned(idx, s->n_layers, kElemAlign) ||
+      !all_aligned(n_kept, s->n_layers, kElemAlign))
+    return BKV_EINVAL;
   if (s->capacity > 64 * kSelectThreads) return BKV_EUNSUPPORTED;
   const size_t sb = layer_bytes(s, s->n_kv_heads, s->capacity, 1, 4);
   const size_t ib = layer_bytes(s, s->n_kv_heads, budget, 1, 4);
@@ -187,6 +206,10 @@ bkv_status check_compact_args(const bkv_shape* s, const void* const* k, const vo
   if (static_cast<long long>(budget) * (s->head_dim / 8) >= (1LL << 30)) return BKV_EUNSUPPORTED;
   if (!all_set(k, s->n_layers) || !all_set(v, s->n_layers) || !all_set(idx, s->n_layers) ||
       !all_set(n_kept, s->n_layers) || !all_set(k_out, s->n_layers) || !all_set(v_out, s->n_layers))
+    return BKV_EINVAL;
+  if (!all_aligned(k, s->n_layers, kRowAlign) || !all_aligned(v, s->n_layers, kRowAlign) ||
+      !all_aligned(k_out, s->n_layers, kRowAlign) || !all_aligned(v_out, s->n_layers, kRowAlign) ||
+      !all_aligned(idx, s->n_layers, kElemAlign) || !all_aligned(n_kept, s->n_layers, kElemAlign))
     return BKV_EINVAL;
   const size_t kb = layer_bytes(s, s->n_kv_heads, s->capacity, s->head_dim, 2);
   const size_t ob = layer_bytes(s, s->n_kv_heads, out_capacity, s->head_dim, 2);
@@ -237,7 +260,7 @@ using namespace bkv;
 
 extern "C" {
 
-const char* bkv_status_string(bkv_status status) {
+const char* bkv_status_string(int32_t status) {
   switch (status) {
     case BKV_OK: return "BKV_OK: success";
     case BKV_EINVAL: return "BKV_EINVAL: invalid argument";
@@ -267,7 +290,7 @@ bkv_status bkv_score(const bkv_shape* shape, const void* const* k, const void* c
 
 bkv_status bkv_score_agg(const bkv_shape* shape, const void* const* k, const void* const* q, int32_t q_len,
                          int32_t window, const void* const* beacons, const int32_t* const* n_beacons, int32_t nb_max,
-                         bkv_aggregation aggregation, float* const* scores, void* workspace, size_t workspace_bytes,
+                         int32_t aggregation, float* const* scores, void* workspace, size_t workspace_bytes,
                          hipStream_t stream) {
   if (aggregation != BKV_AGG_MAX && aggregation != BKV_AGG_MEAN) return BKV_EINVAL;
   bkv_status st = check_score_args(shape, k, q, q_len, window, beacons, n_beacons, nb_max, scores);
@@ -390,7 +413,7 @@ bkv_status bkv_update_beacons(const bkv_shape* shape, const void* const* beacons
 
 bkv_status bkv_update_beacons_policy(const bkv_shape* shape, const void* const* beacons_in,
                                      const int32_t* const* n_in, int32_t nb_max, const void* const* q_new,
-                                     int32_t q_len, int32_t t_new, bkv_beacon_policy policy,
+                                     int32_t q_len, int32_t t_new, int32_t policy,
                                      void* const* beacons_out, int32_t* const* n_out, hipStream_t stream) {
   if (policy != BKV_BEACON_FPS && policy != BKV_BEACON_INITIAL) return BKV_EINVAL;
   bkv_status st = check_shape(shape);
@@ -400,6 +423,10 @@ bkv_status bkv_update_beacons_policy(const bkv_shape* shape, const void* const* 
       !all_set(beacons_out, shape->n_layers) || !all_set(n_out, shape->n_layers))
     return BKV_EINVAL;
   if (t_new > 0 && !all_set(q_new, shape->n_layers)) return BKV_EINVAL;
+  if (!all_aligned(beacons_in, shape->n_layers, kRowAlign) || !all_aligned(beacons_out, shape->n_layers, kRowAlign) ||
+      !all_aligned(n_in, shape->n_layers, kElemAlign) || !all_aligned(n_out, shape->n_layers, kElemAlign) ||
+      (t_new > 0 && !all_aligned(q_new, shape->n_layers, kRowAlign)))
+    return BKV_EINVAL;
   const int g = shape->n_q_heads / shape->n_kv_heads;
   const long long pool_max = nb_max + static_cast<long long>(g) * t_new;
   if (policy == BKV_BEACON_FPS && pool_max > BKV_MAX_POOL) return BKV_EUNSUPPORTED;
@@ -486,6 +513,9 @@ bkv_status bkv_decode_attention(const bkv_shape* shape, const void* const* q, co
   if (g > kDecodeMaxGroup) return BKV_EUNSUPPORTED;
   if (!all_set(q, shape->n_layers) || !all_set(k, shape->n_layers) || !all_set(v, shape->n_layers) ||
       !all_set(out, shape->n_layers))
+    return BKV_EINVAL;
+  if (!all_aligned(q, shape->n_layers, kRowAlign) || !all_aligned(k, shape->n_layers, kRowAlign) ||
+      !all_aligned(v, shape->n_layers, kRowAlign) || !all_aligned(out, shape->n_layers, kElemAlign))
     return BKV_EINVAL;
   const DecodeWs ws = decode_ws(shape);
   if (workspace == nullptr || workspace_bytes < ws.total || reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)

@@ -1,7 +1,7 @@
 // Beacon maintenance by continual farthest-point sampling on cosine distance
 // (BeaconKV page, Figure 7 caption "Continual FPS"; Abstract: beacons represent the
-// global query clusters without keeping the query history; Figure 4 (a): cosine
-// similarity between queries).
+// global query clusters without keeping the query history; Figure 4 (a): queries are
+// compared by their cosine).
 //
 // Pools of up to 768 rows (continual updates): one workgroup per unit, one thread per pool
 // row (the workgroup is the largest pool rounded up to whole waves, so two units share a CU

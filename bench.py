@@ -37,7 +37,7 @@ def parse():
     p.add_argument("--workload", default="qwen7b_16k")
     p.add_argument("--cpu-units", type=int, default=-1,
                    help="at most this many units in the CPU-oracle sample (0: skip; -1: no limit; "
-                        "the sample stops after about 15 s of oracle time either way)")
+                        "each pool process stops after about 15 s of oracle work either way)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device copy five times (a known-size reference for the "
                             "FETCH_SIZE / WRITE_SIZE counters)")
@@ -132,46 +132,107 @@ def score_traffic(workload):
     return float(vals["traffic_bytes_per_call"])
 
 
-def cpu_baseline(w, n_units, budget_s=15.0):
-    """Time the CPU oracle on a bounded sample of units of the same workload: units in a
-    seeded random order until about budget_s seconds of oracle time or n_units units
-    (-1: no unit limit)."""
-    import numpy as np
+# ---- CPU oracle baseline ---------------------------------------------------------------------
+# The float64 oracle runs units (layer, sequence, KV head) in a process pool, one BLAS thread
+# per process.  The pool is forked before anything touches the GPU (its processes hold no GPU
+# state) and is sized to the host cores this job may use, at most CPU_POOL_MAX (the CPU share
+# of one GPU on the measurement host).
+
+CPU_POOL_MAX = 16
+
+
+def cpu_pool_size():
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    return max(1, min(cores, CPU_POOL_MAX))
+
+
+def _oracle_worker_init():
     import threadpoolctl
+    import torch
+    torch.set_num_threads(1)
+    threadpoolctl.threadpool_limits(1)
+
+
+def _oracle_units(job):
+    """Worker: build the inputs of its units (untimed), wait for every worker, then time the
+    oracle over them.  Returns (cached rows, oracle seconds, seconds of each unit)."""
+    w, units, barrier = job
     from synth import unit_inputs, bf16_bits
     from oracle import bkv_oracle as O
-    rng = np.random.default_rng(1)
-    order = rng.permutation(w.units)
-    if n_units > 0:
-        order = order[:n_units]
-    t_total = 0.0
-    keys_total = 0
-    done = 0
-    per_layer = w.batch * w.n_kv_heads
-    for u_id in order:
-        l, rem = divmod(int(u_id), per_layer)
-        b, h = divmod(rem, w.n_kv_heads)
+    prepared = []
+    for l, b, h in units:
         u = unit_inputs(w, l, b, h, "cpu")
-        kb, vb, qb, bb = bf16_bits(u["k"]), bf16_bits(u["v"]), bf16_bits(u["q"]), bf16_bits(u["beacons"])
-        t0 = time.perf_counter()
-        nb = u["nb"]
+        prepared.append((bf16_bits(u["k"]), bf16_bits(u["v"]), bf16_bits(u["q"]), bf16_bits(u["beacons"]),
+                         u["nb"], u["L"]))
+    barrier.wait()
+    t0 = time.perf_counter()
+    rows = 0
+    each = []
+    for kb, vb, qb, bb, nb, L in prepared:
+        t1 = time.perf_counter()
         if w.runs_fps:
             bb, nb, _ = O.update_beacons(bb, nb, qb[:, w.q_len - w.t_new:], w.nb_max)
         O.compress_unit(kb, vb, qb, bb, nb, w.window, w.budget)
-        t_total += time.perf_counter() - t0
-        keys_total += u["L"]
-        done += 1
-        if t_total >= budget_s:
-            break
-    # tokens/s: a token is compressed once all layers x KV heads of its sequence are done
-    rows_per_s = keys_total / t_total
-    tokens_per_s = rows_per_s / (w.n_layers * w.n_kv_heads)
-    info = threadpoolctl.threadpool_info()
-    threads = max([i.get("num_threads", 1) for i in info] or [1])
-    return {"value": tokens_per_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} of {w.units} (layer, sequence, KV head) units of {w.name} in seeded random order "
-                      f"(stop after ~{budget_s:.0f} s), {keys_total} cached rows, {t_total:.1f} s of float64 NumPy "
-                      f"(beacon update, scores, top-K, compaction); rows/s divided by layers x KV heads"}
+        rows += L
+        each.append(time.perf_counter() - t1)
+    return rows, time.perf_counter() - t0, each
+
+
+class CpuBaseline:
+    """The oracle's pool, created at start-up (before the GPU is initialised)."""
+
+    def __init__(self, size):
+        import multiprocessing as mp
+        self.size = size
+        self.ctx = mp.get_context("fork")
+        self.manager = self.ctx.Manager()
+        self.pool = self.ctx.Pool(size, initializer=_oracle_worker_init)
+
+    def close(self):
+        self.pool.close()
+        self.pool.join()
+        self.manager.shutdown()
+
+    def run(self, w, n_units, budget_s=15.0):
+        """A bounded sample of the workload's units in seeded random order: three units
+        timed alone first (their median is the single-process seconds per unit), then about
+        budget_s seconds of oracle work per process, all processes together.  tokens/s = rows
+        per wall second of the pooled run / (layers x KV heads)."""
+        import numpy as np
+        rng = np.random.default_rng(1)
+        per_layer = w.batch * w.n_kv_heads
+        order = []
+        for u_id in rng.permutation(w.units):
+            l, rem = divmod(int(u_id), per_layer)
+            order.append((l, *divmod(rem, w.n_kv_heads)))
+        if n_units > 0:
+            order = order[:n_units]
+        calib = order[:3]
+        rows1, t1, each = self.pool.apply(_oracle_units, ((w, calib, self.manager.Barrier(1)),))
+        per_unit = float(np.median(each))
+        rest = order[len(calib):]
+        k = max(1, min(int(budget_s / max(per_unit, 1e-6)), -(-len(rest) // self.size)))
+        shares = [rest[i * k:(i + 1) * k] for i in range(self.size)]
+        shares = [sh for sh in shares if sh]
+        if shares:
+            barrier = self.manager.Barrier(len(shares))
+            res = self.pool.map(_oracle_units, [(w, sh, barrier) for sh in shares], chunksize=1)
+        else:
+            shares = [calib]
+            res = [(rows1, t1, each)]
+        rows = sum(r[0] for r in res)
+        wall = max(r[1] for r in res)
+        done = sum(len(sh) for sh in shares)
+        tokens_per_s = rows / wall / (w.n_layers * w.n_kv_heads)
+        return {"value": tokens_per_s, "unit": "tokens/s", "cores": len(shares), "kind": "oracle",
+                "os_cpu_count": os.cpu_count(), "pool_size": self.size, "processes_used": len(shares),
+                "single_process_s_per_unit": round(per_unit, 4),
+                "single_process_s_all_units": round(per_unit * w.units, 1),
+                "sample": f"{done} of {w.units} (layer, sequence, KV head) units of {w.name} in seeded random order, "
+                          f"{len(shares)} processes x up to {k} units (~{budget_s:.0f} s each, one BLAS thread per "
+                          f"process), {rows} cached rows in {wall:.1f} s wall; float64 NumPy beacon update, scores, "
+                          f"top-K and compaction; inputs built before the timed region; rows/s divided by "
+                          f"layers x KV heads"}
 
 
 def decode_bench(args, w, log):
@@ -294,6 +355,7 @@ def main():
         return steady_state(args, w, log)
     if args.decode:
         return decode_bench(args, w, log)
+    cpu = CpuBaseline(cpu_pool_size()) if args.cpu_units != 0 else None
     if args.window is not None:
         w = w.replace(window=args.window)
     if args.beacons is not None:
@@ -405,9 +467,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    if args.cpu_units != 0:
-        log("[bench] CPU oracle on a sample ...")
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_units)
+    if cpu is not None:
+        log(f"[bench] CPU oracle on a sample ({cpu.size} processes) ...")
+        out["cpu_baseline"] = cpu.run(w, args.cpu_units)
+        cpu.close()
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

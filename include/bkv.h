@@ -40,6 +40,9 @@
  *   kept counts    int32 [batch][n_kv_heads]
  *   compacted K, V bf16  [batch][n_kv_heads][budget][head_dim]
  * Row j of a cache is valid for j < L_b = min(seq_len[b], capacity).
+ * Alignment: every bf16 array above (each layer's pointer) starts on a 16-byte boundary,
+ * since the kernels move rows in 16-byte pieces; fp32 and int32 arrays (seq_len
+ * included) on a 4-byte boundary.  A misaligned pointer is BKV_EINVAL.
  *
  * Memory and ordering.  Every pointer is device memory owned by the caller unless stated
  * otherwise.  The library never allocates, frees or synchronises; it keeps no pointer
@@ -72,7 +75,8 @@ extern "C" {
 
 typedef enum bkv_status {
   BKV_OK = 0,
-  BKV_EINVAL = -1,        /* null pointer, non-positive size, window > budget, ...     */
+  BKV_EINVAL = -1,        /* null or misaligned pointer, non-positive size,            */
+                          /* window > budget, ...                                      */
   BKV_EUNSUPPORTED = -2,  /* valid but outside what the kernels support (head_dim,      */
                           /* observation rows, beacon pool size)                        */
   BKV_EALIAS = -3,        /* an output overlaps an input, the workspace or an output    */
@@ -97,8 +101,10 @@ typedef struct bkv_shape {
  * (pools above 768 rows, e.g. a whole query history, take a slower streaming kernel). */
 #define BKV_MAX_POOL 16384
 
-/* Human-readable name of a status code (static string, never NULL). */
-const char* bkv_status_string(bkv_status status);
+/* Human-readable name of a status code, a bkv_status value (static string, never NULL;
+ * any other value names an unknown status).  Enumerated arguments throughout this header
+ * are passed as int32_t, so a caller may pass any value and get an error back. */
+const char* bkv_status_string(int32_t status);
 
 /* Library version, e.g. "0.2.0" (static string). */
 const char* bkv_version(void);
@@ -161,7 +167,7 @@ bkv_status bkv_update_beacons_policy(const bkv_shape* shape,
                                      const void* const* beacons_in, const int32_t* const* n_in,
                                      int32_t nb_max,
                                      const void* const* q_new, int32_t q_len, int32_t t_new,
-                                     bkv_beacon_policy policy,
+                                     int32_t policy /* bkv_beacon_policy */,
                                      void* const* beacons_out, int32_t* const* n_out,
                                      hipStream_t stream);
 
@@ -220,7 +226,7 @@ bkv_status bkv_score_agg(const bkv_shape* shape,
                          const void* const* k,
                          const void* const* q, int32_t q_len, int32_t window,
                          const void* const* beacons, const int32_t* const* n_beacons, int32_t nb_max,
-                         bkv_aggregation aggregation,
+                         int32_t aggregation /* bkv_aggregation */,
                          float* const* scores,
                          void* workspace, size_t workspace_bytes,
                          hipStream_t stream);

@@ -131,9 +131,22 @@ def check_selection(keep_gpu: np.ndarray, s_gpu: np.ndarray, s_or: np.ndarray, L
     return {"swaps": float(extra.size), "gap": gap}
 
 
-def check_unit(w: Workload, ev: CompressionEvent, layer: int, b: int, h: int) -> Dict[str, float]:
-    """One unit's beacons, scores (under the event's aggregation), selection and compaction."""
-    u = unit_inputs(w, layer, b, h, "cpu")
+def unit_from_inputs(w: Workload, inputs: Dict[str, List[torch.Tensor]], layer: int, b: int, h: int):
+    """The unit's slices of explicit input tensors (e.g. generator output with planted
+    rows), in the layout `unit_inputs` returns: the oracle then sees exactly the bits the
+    GPU consumed."""
+    G = w.group
+    L = int(inputs["seq_len"][b].item())
+    return {"k": inputs["k"][layer][b, h, :L].cpu(), "v": inputs["v"][layer][b, h, :L].cpu(),
+            "q": inputs["q"][layer][b, h * G:(h + 1) * G].cpu(), "beacons": inputs["beacons"][layer][b, h].cpu(),
+            "nb": int(inputs["n_beacons"][layer][b, h].item()), "L": L}
+
+
+def check_unit(w: Workload, ev: CompressionEvent, layer: int, b: int, h: int,
+               inputs: Optional[Dict[str, List[torch.Tensor]]] = None) -> Dict[str, float]:
+    """One unit's beacons, scores (under the event's aggregation), selection and compaction.
+    The unit's inputs are regenerated from the workload's seeds, or taken from `inputs`."""
+    u = unit_inputs(w, layer, b, h, "cpu") if inputs is None else unit_from_inputs(w, inputs, layer, b, h)
     L = u["L"]
     kb, vb, qb, bcb = bf16_bits(u["k"]), bf16_bits(u["v"]), bf16_bits(u["q"]), bf16_bits(u["beacons"])
     stats: Dict[str, float] = {}
@@ -177,11 +190,12 @@ def check_unit(w: Workload, ev: CompressionEvent, layer: int, b: int, h: int) ->
     return stats
 
 
-def check_units(w: Workload, ev: CompressionEvent, units: Sequence[Tuple[int, int, int]]) -> Dict[str, float]:
+def check_units(w: Workload, ev: CompressionEvent, units: Sequence[Tuple[int, int, int]],
+                inputs: Optional[Dict[str, List[torch.Tensor]]] = None) -> Dict[str, float]:
     worst = {"score_rel_max": 0.0, "swaps": 0.0, "gap": 0.0}
     for (l, b, h) in units:
         t0 = time.time()
-        st = check_unit(w, ev, l, b, h)
+        st = check_unit(w, ev, l, b, h, inputs)
         for k, v in st.items():
             worst[k] = max(worst.get(k, 0.0), v)
         log(f"  unit (layer {l}, b {b}, h {h}) ok in {time.time() - t0:.1f}s: {st}")

@@ -270,3 +270,39 @@ def test_outputs_may_not_overlap_anything_the_call_touches():
                                     None) == bkv.BKV_EALIAS                                # out over the lengths
     assert lib.bkv_decode_attention(ctypes.byref(s), qs, ks, vs, arr(FAKE + (4 << 36)), FAKE + (1 << 36), need,
                                     None) == bkv.BKV_EALIAS                                # workspace over q
+
+
+def test_misaligned_pointers_are_rejected():
+    """bf16 rows move in 16-byte pieces, fp32 / int32 arrays element by element: a layer
+    pointer off those boundaries is BKV_EINVAL at every entry point, before any launch."""
+    lib = bkv.load()
+    s = shape()
+    # score: K, queries, beacons on 16 bytes; scores and beacon counts on 4
+    for kw in (dict(k=arr(FAKE + (1 << 36) + 8)), dict(q=arr(FAKE + (2 << 36) + 2)),
+               dict(bc=arr(FAKE + (3 << 36) + 4)), dict(nb=arr(FAKE + (4 << 36) + 2)),
+               dict(sc=arr(FAKE + (5 << 36) + 2)), dict(s=shape(seq_len=FAKE + 2))):
+        assert score_call(**kw) == bkv.BKV_EINVAL, kw
+    # select: scores, idx, n_kept on 4 bytes
+    sc, idx, nk = arr(FAKE), arr(FAKE + (1 << 36)), arr(FAKE + (2 << 36))
+    for a, b, c in ((arr(FAKE + 2), idx, nk), (sc, arr(FAKE + (1 << 36) + 1), nk), (sc, idx, arr(FAKE + (2 << 36) + 3))):
+        assert lib.bkv_select_topk(ctypes.byref(s), a, 64, 8, b, c, None, 0, None) == bkv.BKV_EINVAL
+    # compact: K, V, outputs on 16 bytes
+    k, v = arr(FAKE), arr(FAKE + (1 << 36))
+    idx, nk = arr(FAKE + (2 << 36)), arr(FAKE + (3 << 36))
+    ko, vo = arr(FAKE + (4 << 36)), arr(FAKE + (5 << 36))
+    assert lib.bkv_compact(ctypes.byref(s), arr(FAKE + 8), v, idx, nk, 64, ko, vo, None) == bkv.BKV_EINVAL
+    assert lib.bkv_compact(ctypes.byref(s), k, v, idx, nk, 64, ko, arr(FAKE + (5 << 36) + 4), None) == bkv.BKV_EINVAL
+    assert lib.bkv_compact(ctypes.byref(s), k, v, arr(FAKE + (2 << 36) + 2), nk, 64, ko, vo, None) == bkv.BKV_EINVAL
+    # beacon update: beacon rows and new queries on 16 bytes, counts on 4
+    bi, ni, qn = arr(FAKE), arr(FAKE + (1 << 36)), arr(FAKE + (2 << 36))
+    bo, no = arr(FAKE + (3 << 36)), arr(FAKE + (4 << 36))
+    f = lib.bkv_update_beacons
+    assert f(ctypes.byref(s), arr(FAKE + 4), ni, 16, qn, 128, 128, bo, no, None) == bkv.BKV_EINVAL
+    assert f(ctypes.byref(s), bi, ni, 16, arr(FAKE + (2 << 36) + 8), 128, 128, bo, no, None) == bkv.BKV_EINVAL
+    assert f(ctypes.byref(s), bi, ni, 16, qn, 128, 128, arr(FAKE + (3 << 36) + 2), no, None) == bkv.BKV_EINVAL
+    assert f(ctypes.byref(s), bi, ni, 16, qn, 128, 128, bo, arr(FAKE + (4 << 36) + 2), None) == bkv.BKV_EINVAL
+    # decode: q, K, V on 16 bytes
+    out, ws = arr(FAKE + (3 << 36)), FAKE + (1 << 40)
+    d = lib.bkv_decode_attention
+    assert d(ctypes.byref(s), arr(FAKE + (4 << 36) + 2), k, v, out, ws, 1 << 40, None) == bkv.BKV_EINVAL
+    assert d(ctypes.byref(s), arr(FAKE + (4 << 36)), arr(FAKE + 8), v, out, ws, 1 << 40, None) == bkv.BKV_EINVAL

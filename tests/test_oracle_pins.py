@@ -33,6 +33,28 @@ def _bits(x: np.ndarray) -> np.ndarray:
 
 
 # ------------------------------------------------------------------------------------------------
+# input decoding
+# ------------------------------------------------------------------------------------------------
+
+def test_bf16_decoding_matches_torch_on_every_bit_pattern():
+    """All 65,536 bf16 patterns decode to the value torch's own bf16 -> float64 conversion
+    gives (signed zeros, subnormals, infinities and the sign of every value included; NaN
+    patterns decode to NaN)."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = O.bf16_to_f64(bits)
+    want = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert nan.sum() == 2 * (2 ** 7 - 1)                  # exponent all ones, mantissa non-zero
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+    # shape is kept and a few patterns by hand: 1.0, -2.0, smallest subnormal, largest finite
+    hand = O.bf16_to_f64(np.array([[0x3F80, 0xC000], [0x0001, 0x7F7F]], dtype=np.uint16))
+    assert hand.shape == (2, 2)
+    assert hand.tolist() == [[1.0, -2.0], [2.0 ** -133, (2 - 2 ** -7) * 2.0 ** 127]]
+
+
+# ------------------------------------------------------------------------------------------------
 # scores
 # ------------------------------------------------------------------------------------------------
 

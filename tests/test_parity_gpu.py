@@ -116,7 +116,7 @@ def test_mean_aggregation(case):
 
 # Table 1's splits of the 32 observation slots per query step between recent queries and
 # beacons (n_recent, n_beacon), on the serving shape with the continual-FPS update.
-SPLITS = [(1, 31), (8, 24), (28, 4)]
+SPLITS = [(1, 31), (4, 28), (8, 24), (16, 16), (24, 8), (28, 4)]
 
 
 @pytest.mark.parametrize("n_recent,n_beacon", SPLITS)
