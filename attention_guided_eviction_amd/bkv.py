@@ -13,6 +13,7 @@ Operations (BeaconKV page, thelatestinai.com/papers/2609.04971):
   select_topk     top-K under the budget, recent window always kept (Figure 5 (c))
   compact         gather of the kept K/V rows (Abstract)
   compress        score + select_topk + compact
+  compress_static the same with no workspace (the library's static device scratch)
 """
 from __future__ import annotations
 
@@ -40,13 +41,15 @@ EXPORTS = ["bkv_status_string", "bkv_version", "bkv_last_error", "bkv_update_bea
            "bkv_score_workspace_bytes",
            "bkv_score", "bkv_score_agg", "bkv_select_workspace_bytes", "bkv_select_topk", "bkv_compact",
            "bkv_compact_into", "bkv_decode_workspace_bytes", "bkv_decode_attention",
-           "bkv_compress_workspace_bytes", "bkv_compress"]
+           "bkv_compress_workspace_bytes", "bkv_compress", "bkv_compress_static"]
+# Bytes of bkv_compress_static's device scratch (BKV_STATIC_SCRATCH_BYTES).
+STATIC_SCRATCH_BYTES = 32 << 20
 
 
 class BkvError(RuntimeError):
     def __init__(self, status: int, what: str):
         msg = f"{what}: {status_string(status)} ({status})"
-        if status == BKV_EHIP:
+        if status == BKV_EHIP or (status == BKV_EUNSUPPORTED and what == "bkv_compress_static"):
             msg += " -- " + load().bkv_last_error().decode()
         super().__init__(msg)
         self.status = status
@@ -105,6 +108,9 @@ def load() -> ctypes.CDLL:
     lib.bkv_compress.restype = ctypes.c_int
     lib.bkv_compress.argtypes = [P(_Shape), arr, arr, arr, i32, i32, arr, arr, i32, i32, arr, arr, arr,
                                  arr, arr, vp, sz, vp]
+    lib.bkv_compress_static.restype = ctypes.c_int
+    lib.bkv_compress_static.argtypes = [P(_Shape), arr, arr, arr, i32, i32, arr, arr, i32, i32, arr, arr, arr,
+                                        arr, arr, vp]
     _lib = lib
     return lib
 
@@ -341,11 +347,9 @@ def compress_workspace_bytes(s: CacheShape, window: int, nb_max: int, budget: in
     return int(load().bkv_compress_workspace_bytes(ctypes.byref(s.c()), window, nb_max, budget))
 
 
-def prepare_compress(s: CacheShape, k, v, q, q_len: int, window: int, beacons, n_beacons, nb_max: int,
-                     budget: int, scores, idx, n_kept, k_out, v_out, workspace: Optional[torch.Tensor]) -> Call:
-    lib = load()
+def _compress_args(s: CacheShape, k, v, q, q_len, window, beacons, n_beacons, nb_max, budget, scores, idx, n_kept,
+                   k_out, v_out):
     B, Hkv, D, cap, n = s.batch, s.n_kv_heads, s.head_dim, s.capacity, s.n_layers
-    shape = s.c()
     kp, qp, bp, nbp = _score_inputs(s, k, q, q_len, window, beacons, n_beacons, nb_max)
     vp = _layers(v, n, torch.bfloat16, (B, Hkv, cap, D), "v")
     sp = _layers(scores, n, torch.float32, (B, Hkv, cap), "scores")
@@ -353,11 +357,31 @@ def prepare_compress(s: CacheShape, k, v, q, q_len: int, window: int, beacons, n
     np_ = _layers(n_kept, n, torch.int32, (B, Hkv), "n_kept")
     ko = _layers(k_out, n, torch.bfloat16, (B, Hkv, budget, D), "k_out")
     vo = _layers(v_out, n, torch.bfloat16, (B, Hkv, budget, D), "v_out")
+    return (kp, vp, qp, q_len, window, bp, nbp, nb_max, budget, sp, ip, np_, ko, vo)
+
+
+def prepare_compress(s: CacheShape, k, v, q, q_len: int, window: int, beacons, n_beacons, nb_max: int,
+                     budget: int, scores, idx, n_kept, k_out, v_out, workspace: Optional[torch.Tensor]) -> Call:
+    lib = load()
+    shape = s.c()
+    args = _compress_args(s, k, v, q, q_len, window, beacons, n_beacons, nb_max, budget, scores, idx, n_kept,
+                          k_out, v_out)
     need = int(lib.bkv_compress_workspace_bytes(ctypes.byref(shape), window, nb_max, budget))
     wp, wn = _workspace(workspace, need)
-    args = (ctypes.byref(shape), kp, vp, qp, q_len, window, bp, nbp, nb_max, budget, sp, ip, np_, ko, vo, wp, wn)
-    return Call(lib.bkv_compress, args, "bkv_compress",
+    return Call(lib.bkv_compress, (ctypes.byref(shape),) + args + (wp, wn), "bkv_compress",
                 (shape, s.seq_len, k, v, q, beacons, n_beacons, scores, idx, n_kept, k_out, v_out, workspace))
+
+
+def prepare_compress_static(s: CacheShape, k, v, q, q_len: int, window: int, beacons, n_beacons, nb_max: int,
+                            budget: int, scores, idx, n_kept, k_out, v_out) -> Call:
+    """bkv_compress_static: bkv_compress without a workspace (nothing is allocated; calls on
+    one device must not overlap in time)."""
+    lib = load()
+    shape = s.c()
+    args = _compress_args(s, k, v, q, q_len, window, beacons, n_beacons, nb_max, budget, scores, idx, n_kept,
+                          k_out, v_out)
+    return Call(lib.bkv_compress_static, (ctypes.byref(shape),) + args, "bkv_compress_static",
+                (shape, s.seq_len, k, v, q, beacons, n_beacons, scores, idx, n_kept, k_out, v_out))
 
 
 def compress(s: CacheShape, k, v, q, q_len: int, window: int, beacons, n_beacons, nb_max: int, budget: int,
@@ -365,3 +389,10 @@ def compress(s: CacheShape, k, v, q, q_len: int, window: int, beacons, n_beacons
     """One compression event over every layer: score, select, compact (bkv_compress)."""
     prepare_compress(s, k, v, q, q_len, window, beacons, n_beacons, nb_max, budget, scores, idx, n_kept, k_out,
                      v_out, workspace)(stream)
+
+
+def compress_static(s: CacheShape, k, v, q, q_len: int, window: int, beacons, n_beacons, nb_max: int,
+                    budget: int, scores, idx, n_kept, k_out, v_out, stream=None) -> None:
+    """One compression event with no workspace argument (bkv_compress_static)."""
+    prepare_compress_static(s, k, v, q, q_len, window, beacons, n_beacons, nb_max, budget, scores, idx, n_kept,
+                            k_out, v_out)(stream)

@@ -1,6 +1,7 @@
 // Host side of the libbkv C ABI (include/bkv.h): argument checks, workspace sizing,
 // splitting long models into launches of at most kMaxLayers layers, and launches.
-// Nothing here allocates, frees or synchronises.
+// Nothing here allocates, frees or synchronises (the partials of bkv_compress_static sit
+// in a static device array that the code object brings).
 #include <math.h>
 #include <stdio.h>
 #include <string.h>
@@ -9,6 +10,14 @@
 #include <vector>
 
 #include "bkv_internal.h"
+
+// Statistics partials of bkv_compress_static: one copy of this array per device,
+// allocated when the code object is loaded on that device and held until the process
+// ends.  In host code the name stands for a host-side shadow, never for device memory:
+// the device address comes from hipGetSymbolAddress, taken once per device with that
+// device current (static_scratch below).
+constexpr size_t kStaticScratchBytes = BKV_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 
 namespace bkv {
 namespace {
@@ -119,20 +128,28 @@ struct ScoreWs {
   size_t part_bytes, total;
 };
 
-// Statistics partials of the largest launch: launches of kMaxLayers layers and one of the
-// remaining layers run one after another on the stream and reuse the workspace.
-ScoreWs score_ws(const bkv_shape* s, int window, int nb_max) {
+// Statistics partials of the largest launch when the score call goes out in launches of
+// at most `layers` layers and `seqs` sequences (the launches run one after another on
+// the stream and reuse the workspace).  Slots per unit depend on the layers of a launch
+// only, so the largest launch is one of `seqs` sequences and either `layers` layers or
+// the remainder.
+ScoreWs score_ws(const bkv_shape* s, int window, int nb_max, int layers, int seqs) {
   ScoreWs w{};
   const size_t obs = static_cast<size_t>(obs_pad_of(s, window, nb_max));
   size_t cells = 0;
-  for (int nl : {layers_per_launch(s), s->n_layers % kMaxLayers}) {
+  for (int nl : {layers, s->n_layers % layers}) {
     if (nl == 0) continue;
-    const size_t units = static_cast<size_t>(nl) * s->batch * s->n_kv_heads;
+    const size_t units = static_cast<size_t>(nl) * seqs * s->n_kv_heads;
     cells = std::max(cells, units * static_cast<size_t>(score_slots(s->capacity, nl, s->n_kv_heads)));
   }
   w.part_bytes = align_up(cells * obs * sizeof(float));
   w.total = 2 * w.part_bytes;
   return w;
+}
+
+// The default grouping: kMaxLayers layers (or all of them) and the whole batch per launch.
+ScoreWs score_ws(const bkv_shape* s, int window, int nb_max) {
+  return score_ws(s, window, nb_max, layers_per_launch(s), s->batch);
 }
 
 bkv_status check_score_args(const bkv_shape* s, const void* const* k, const void* const* q, int32_t q_len,
@@ -227,6 +244,52 @@ bkv_status check_compact_args(const bkv_shape* s, const void* const* k, const vo
 
 bkv_status hip_status(hipError_t e) { return e == hipSuccess ? BKV_OK : BKV_EHIP; }
 
+// The score call's launches: groups of at most `layers` layers and `seqs` sequences, in
+// layer-major order, all sharing the partials at `ws_base` (laid out as `ws` says).  A
+// group of sequences b0 .. b0+n-1 is the same call on the arrays' sub-blocks that start at
+// sequence b0 (every array is sequence-major) and on seq_len + b0.  Arguments were
+// checked by check_score_args.
+bkv_status run_score(const bkv_shape* shape, const void* const* k, const void* const* q, int32_t q_len,
+                     int32_t window, const void* const* beacons, const int32_t* const* n_beacons, int32_t nb_max,
+                     int mean, float* const* scores, char* ws_base, const ScoreWs& ws, int layers, int seqs,
+                     hipStream_t stream) {
+  ScoreArgs a;
+  memset(&a, 0, sizeof(a));
+  a.part_m = reinterpret_cast<float*>(ws_base);
+  a.part_z = reinterpret_cast<float*>(ws_base + ws.part_bytes);
+  a.n_q_heads = shape->n_q_heads;
+  a.n_kv_heads = shape->n_kv_heads;
+  a.group = shape->n_q_heads / shape->n_kv_heads;
+  a.capacity = shape->capacity;
+  a.q_len = q_len;
+  a.window = window;
+  a.nb_max = nb_max;
+  a.obs_pad = obs_pad_of(shape, window, nb_max);
+  a.scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(shape->head_dim)));
+  a.mean = mean;
+  const size_t hkv = static_cast<size_t>(shape->n_kv_heads), hq = static_cast<size_t>(shape->n_q_heads);
+  const size_t d = static_cast<size_t>(shape->head_dim);
+  for (int l0 = 0; l0 < shape->n_layers; l0 += layers) {
+    const int nl = std::min(layers, shape->n_layers - l0);
+    for (int b0 = 0; b0 < shape->batch; b0 += seqs) {
+      const size_t b = static_cast<size_t>(b0);
+      a.batch = std::min(seqs, shape->batch - b0);
+      a.seq_len = shape->seq_len + b0;
+      for (int i = 0; i < nl; ++i) {
+        const int l = l0 + i;
+        a.k[i] = static_cast<const uint16_t*>(k[l]) + b * hkv * shape->capacity * d;
+        a.q[i] = window > 0 ? static_cast<const uint16_t*>(q[l]) + b * hq * q_len * d : nullptr;
+        a.beacons[i] = nb_max > 0 ? static_cast<const uint16_t*>(beacons[l]) + b * hkv * nb_max * d : nullptr;
+        a.n_beacons[i] = nb_max > 0 ? n_beacons[l] + b * hkv : nullptr;
+        a.scores[i] = scores[l] + b * hkv * shape->capacity;
+      }
+      const bkv_status st = hip_status(launch_score(a, nl, shape->head_dim, stream));
+      if (st != BKV_OK) return st;
+    }
+  }
+  return BKV_OK;
+}
+
 struct DecodeWs {
   size_t m_bytes, o_bytes, total;
   int chunk_keys, chunks;
@@ -246,6 +309,85 @@ DecodeWs decode_ws(const bkv_shape* s) {
 }
 
 thread_local char g_last_error[256] = "no HIP error recorded";
+
+// Arguments of one compression event: those of the three stages, and no output of any
+// stage may overlap another stage's output, an input or the workspace (later stages read
+// the earlier ones' outputs).  `workspace` may be null (the static variant has none).
+bkv_status check_compress_args(const bkv_shape* shape, const void* const* k, const void* const* v,
+                               const void* const* q, int32_t q_len, int32_t window, const void* const* beacons,
+                               const int32_t* const* n_beacons, int32_t nb_max, int32_t budget,
+                               float* const* scores, int32_t* const* idx, int32_t* const* n_kept,
+                               void* const* k_out, void* const* v_out, const void* workspace,
+                               size_t workspace_bytes) {
+  bkv_status st = check_score_args(shape, k, q, q_len, window, beacons, n_beacons, nb_max, scores);
+  if (st == BKV_OK) st = check_select_args(shape, scores, budget, window, idx, n_kept);
+  if (st == BKV_OK) st = check_compact_args(shape, k, v, idx, n_kept, budget, budget, k_out, v_out);
+  if (st != BKV_OK) return st;
+  Footprint f;
+  score_inputs(f, shape, k, q, q_len, window, beacons, n_beacons, nb_max);
+  f.in_layers(v, shape->n_layers, layer_bytes(shape, shape->n_kv_heads, shape->capacity, shape->head_dim, 2));
+  f.out_layers(scores, shape->n_layers, layer_bytes(shape, shape->n_kv_heads, shape->capacity, 1, 4));
+  f.out_layers(idx, shape->n_layers, layer_bytes(shape, shape->n_kv_heads, budget, 1, 4));
+  f.out_layers(n_kept, shape->n_layers, layer_bytes(shape, shape->n_kv_heads, 1, 1, 4));
+  f.out_layers(k_out, shape->n_layers, layer_bytes(shape, shape->n_kv_heads, budget, shape->head_dim, 2));
+  f.out_layers(v_out, shape->n_layers, layer_bytes(shape, shape->n_kv_heads, budget, shape->head_dim, 2));
+  if (workspace != nullptr) f.out(workspace, std::min(workspace_bytes, score_ws(shape, window, nb_max).total));
+  return f.clash() ? BKV_EALIAS : BKV_OK;
+}
+
+// ---- the allocation-free compression event ----------------------------------------------
+// Its statistics partials live in the file-scope array `scratch` (top of this file).
+
+PerDeviceOnce g_scratch_once;
+char* g_scratch_addr[kMaxDevices];
+
+hipError_t static_scratch(char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return note_hip_error(e, "compress_static: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return note_hip_error(hipErrorInvalidDevice, "compress_static: device");
+  e = once_per_device(g_scratch_once, [dev] {
+    void* p = nullptr;
+    const hipError_t r = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (r == hipSuccess) g_scratch_addr[dev] = static_cast<char*>(p);
+    return r;
+  });
+  if (e != hipSuccess) return note_hip_error(e, "compress_static: hipGetSymbolAddress");
+  *out = g_scratch_addr[dev];
+  return hipSuccess;
+}
+
+struct ScoreGroups {
+  int layers, seqs;   // per launch; layers == 0: even one layer of one sequence does not fit
+};
+
+// The launch grouping of the static variant: the fewest launches whose partials fit the
+// scratch (ties to more layers per launch); the whole call in the default grouping when
+// that fits.  Sequence groups are evened out over the batch.
+ScoreGroups static_groups(const bkv_shape* s, int window, int nb_max) {
+  ScoreGroups best{0, 0};
+  long long best_launches = 0;
+  for (int nl = layers_per_launch(s); nl >= 1; --nl) {
+    if (score_ws(s, window, nb_max, nl, 1).total > kStaticScratchBytes) continue;
+    int lo = 1, hi = s->batch;   // the most sequences per launch that fit
+    while (lo < hi) {
+      const int mid = lo + (hi - lo + 1) / 2;
+      if (score_ws(s, window, nb_max, nl, mid).total <= kStaticScratchBytes)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    const int seq_groups = (s->batch + lo - 1) / lo;
+    const int seqs = (s->batch + seq_groups - 1) / seq_groups;
+    const long long launches = static_cast<long long>((s->n_layers + nl - 1) / nl) * seq_groups;
+    if (best.layers == 0 || launches < best_launches) {
+      best = ScoreGroups{nl, seqs};
+      best_launches = launches;
+    }
+  }
+  return best;
+}
+
 
 }  // namespace
 
@@ -304,36 +446,8 @@ bkv_status bkv_score_agg(const bkv_shape* shape, const void* const* k, const voi
   f.out_layers(scores, shape->n_layers, layer_bytes(shape, shape->n_kv_heads, shape->capacity, 1, 4));
   f.out(workspace, ws.total);
   if (f.clash()) return BKV_EALIAS;
-  ScoreArgs a;
-  memset(&a, 0, sizeof(a));
-  a.seq_len = shape->seq_len;
-  char* wsp = static_cast<char*>(workspace);
-  a.part_m = reinterpret_cast<float*>(wsp);
-  a.part_z = reinterpret_cast<float*>(wsp + ws.part_bytes);
-  a.batch = shape->batch;
-  a.n_q_heads = shape->n_q_heads;
-  a.n_kv_heads = shape->n_kv_heads;
-  a.group = shape->n_q_heads / shape->n_kv_heads;
-  a.capacity = shape->capacity;
-  a.q_len = q_len;
-  a.window = window;
-  a.nb_max = nb_max;
-  a.obs_pad = obs_pad_of(shape, window, nb_max);
-  a.scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(shape->head_dim)));
-  a.mean = aggregation == BKV_AGG_MEAN ? 1 : 0;
-  for (int l0 = 0; l0 < shape->n_layers; l0 += kMaxLayers) {
-    const int nl = std::min(kMaxLayers, shape->n_layers - l0);
-    for (int i = 0; i < nl; ++i) {
-      a.k[i] = static_cast<const uint16_t*>(k[l0 + i]);
-      a.q[i] = window > 0 ? static_cast<const uint16_t*>(q[l0 + i]) : nullptr;
-      a.beacons[i] = nb_max > 0 ? static_cast<const uint16_t*>(beacons[l0 + i]) : nullptr;
-      a.n_beacons[i] = nb_max > 0 ? n_beacons[l0 + i] : nullptr;
-      a.scores[i] = scores[l0 + i];
-    }
-    st = hip_status(launch_score(a, nl, shape->head_dim, stream));
-    if (st != BKV_OK) return st;
-  }
-  return BKV_OK;
+  return run_score(shape, k, q, q_len, window, beacons, n_beacons, nb_max, aggregation == BKV_AGG_MEAN ? 1 : 0,
+                   scores, static_cast<char*>(workspace), ws, layers_per_launch(shape), shape->batch, stream);
 }
 
 size_t bkv_select_workspace_bytes(const bkv_shape* shape, int32_t budget) {
@@ -476,23 +590,37 @@ bkv_status bkv_compress(const bkv_shape* shape, const void* const* k, const void
                         int32_t nb_max, int32_t budget, float* const* scores, int32_t* const* idx,
                         int32_t* const* n_kept, void* const* k_out, void* const* v_out, void* workspace,
                         size_t workspace_bytes, hipStream_t stream) {
-  bkv_status st = check_score_args(shape, k, q, q_len, window, beacons, n_beacons, nb_max, scores);
-  if (st == BKV_OK) st = check_select_args(shape, scores, budget, window, idx, n_kept);
-  if (st == BKV_OK) st = check_compact_args(shape, k, v, idx, n_kept, budget, budget, k_out, v_out);
+  bkv_status st = check_compress_args(shape, k, v, q, q_len, window, beacons, n_beacons, nb_max, budget, scores, idx,
+                                      n_kept, k_out, v_out, workspace, workspace_bytes);
   if (st != BKV_OK) return st;
-  // the three stages' outputs must not overlap each other either (scores, idx and n_kept
-  // are read by the later stages)
-  Footprint f;
-  score_inputs(f, shape, k, q, q_len, window, beacons, n_beacons, nb_max);
-  f.in_layers(v, shape->n_layers, layer_bytes(shape, shape->n_kv_heads, shape->capacity, shape->head_dim, 2));
-  f.out_layers(scores, shape->n_layers, layer_bytes(shape, shape->n_kv_heads, shape->capacity, 1, 4));
-  f.out_layers(idx, shape->n_layers, layer_bytes(shape, shape->n_kv_heads, budget, 1, 4));
-  f.out_layers(n_kept, shape->n_layers, layer_bytes(shape, shape->n_kv_heads, 1, 1, 4));
-  f.out_layers(k_out, shape->n_layers, layer_bytes(shape, shape->n_kv_heads, budget, shape->head_dim, 2));
-  f.out_layers(v_out, shape->n_layers, layer_bytes(shape, shape->n_kv_heads, budget, shape->head_dim, 2));
-  if (workspace != nullptr) f.out(workspace, std::min(workspace_bytes, score_ws(shape, window, nb_max).total));
-  if (f.clash()) return BKV_EALIAS;
   st = bkv_score(shape, k, q, q_len, window, beacons, n_beacons, nb_max, scores, workspace, workspace_bytes, stream);
+  if (st != BKV_OK) return st;
+  st = bkv_select_topk(shape, scores, budget, window, idx, n_kept, nullptr, 0, stream);
+  if (st != BKV_OK) return st;
+  return bkv_compact(shape, k, v, idx, n_kept, budget, k_out, v_out, stream);
+}
+
+bkv_status bkv_compress_static(const bkv_shape* shape, const void* const* k, const void* const* v,
+                               const void* const* q, int32_t q_len, int32_t window, const void* const* beacons,
+                               const int32_t* const* n_beacons, int32_t nb_max, int32_t budget,
+                               float* const* scores, int32_t* const* idx, int32_t* const* n_kept,
+                               void* const* k_out, void* const* v_out, hipStream_t stream) {
+  bkv_status st = check_compress_args(shape, k, v, q, q_len, window, beacons, n_beacons, nb_max, budget, scores, idx,
+                                      n_kept, k_out, v_out, nullptr, 0);
+  if (st != BKV_OK) return st;
+  const ScoreGroups g = static_groups(shape, window, nb_max);
+  if (g.layers == 0) {
+    snprintf(g_last_error, sizeof(g_last_error),
+             "compress_static: one layer of one sequence needs %zu bytes of statistics partials; the static "
+             "scratch holds %zu",
+             score_ws(shape, window, nb_max, 1, 1).total, kStaticScratchBytes);
+    return BKV_EUNSUPPORTED;
+  }
+  char* base = nullptr;
+  st = hip_status(static_scratch(&base));
+  if (st != BKV_OK) return st;
+  st = run_score(shape, k, q, q_len, window, beacons, n_beacons, nb_max, 0, scores, base,
+                 score_ws(shape, window, nb_max, g.layers, g.seqs), g.layers, g.seqs, stream);
   if (st != BKV_OK) return st;
   st = bkv_select_topk(shape, scores, budget, window, idx, n_kept, nullptr, 0, stream);
   if (st != BKV_OK) return st;

@@ -19,6 +19,7 @@
  *                       (Abstract);
  *   bkv_compact_into    the same into a cache with room for the next decoded tokens;
  *   bkv_compress        bkv_score + bkv_select_topk + bkv_compact in one call;
+ *   bkv_compress_static the same without a workspace, for callers that cannot allocate;
  *   bkv_decode_attention  one decoding step of attention over the (compacted) cache.
  *
  * Conventions shared by every entry point
@@ -46,9 +47,11 @@
  *
  * Memory and ordering.  Every pointer is device memory owned by the caller unless stated
  * otherwise.  The library never allocates, frees or synchronises; it keeps no pointer
- * after returning.  All work is enqueued on `stream` (0 = the null stream) and runs in
- * stream order; results are visible after the caller synchronises.  Calls are
- * thread-safe; concurrent calls must not share output or workspace buffers.
+ * after returning.  (Its one piece of memory of its own is the static scratch array of
+ * bkv_compress_static, part of its code object.)  All work is enqueued on `stream`
+ * (0 = the null stream) and runs in stream order; results are visible after the caller
+ * synchronises.  Calls are thread-safe; concurrent calls must not share output or
+ * workspace buffers, and bkv_compress_static calls on one device must not overlap.
  *
  * Overlap.  No output of a call (nor its workspace) may overlap anything else the call
  * touches: an input of any layer, seq_len, the workspace or another output, counted as
@@ -109,7 +112,8 @@ const char* bkv_status_string(int32_t status);
 /* Library version, e.g. "0.2.0" (static string). */
 const char* bkv_version(void);
 
-/* Which HIP call failed, and how, for this thread's most recent BKV_EHIP (a thread-local
+/* Which HIP call failed, and how, for this thread's most recent BKV_EHIP, or why
+ * bkv_compress_static last returned BKV_EUNSUPPORTED for lack of scratch (a thread-local
  * string valid until the thread's next failing call; "no HIP error recorded" if none). */
 const char* bkv_last_error(void);
 
@@ -311,6 +315,36 @@ bkv_status bkv_compress(const bkv_shape* shape,
                         void* const* k_out, void* const* v_out,
                         void* workspace, size_t workspace_bytes,
                         hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): bkv_compress without a workspace
+ * argument.  Same arguments otherwise, same results, same errors (no BKV_EWORKSPACE).
+ *
+ * The score stage's statistics partials go to a static device array of
+ * BKV_STATIC_SCRATCH_BYTES bytes that the library's code object holds on every device it
+ * is loaded on, until the process ends; the call itself allocates and frees nothing.
+ * Where the default launches' partials would not fit, the score stage goes out in groups
+ * of fewer layers and sequences per launch (same results, more launches).  If even one
+ * layer of one sequence does not fit the call returns BKV_EUNSUPPORTED and enqueues
+ * nothing; bkv_last_error() then says how many bytes it would need.
+ *
+ * Every call on one device shares that device's array, and each call's partials are
+ * written before they are read in the same call, so nothing needs clearing between calls.
+ * Two calls whose work overlaps in time on one device (different streams, different host
+ * threads) race on the array and may return wrong scores: the caller serialises them,
+ * e.g. by issuing them on one stream.
+ * ---------------------------------------------------------------------------------- */
+#define BKV_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+
+bkv_status bkv_compress_static(const bkv_shape* shape,
+                               const void* const* k, const void* const* v,
+                               const void* const* q, int32_t q_len, int32_t window,
+                               const void* const* beacons, const int32_t* const* n_beacons,
+                               int32_t nb_max, int32_t budget,
+                               float* const* scores, int32_t* const* idx, int32_t* const* n_kept,
+                               void* const* k_out, void* const* v_out,
+                               hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
  * One decoding step of attention over a cache (typically the compacted one).

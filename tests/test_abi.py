@@ -44,6 +44,8 @@ def test_header_limits_match_binding():
     text = open(HEADER).read()
     assert int(re.search(r"#define BKV_MAX_OBS (\d+)", text).group(1)) == bkv.MAX_OBS
     assert int(re.search(r"#define BKV_MAX_POOL (\d+)", text).group(1)) == bkv.MAX_POOL
+    mib = int(re.search(r"#define BKV_STATIC_SCRATCH_BYTES \(\(size_t\)(\d+) << 20\)", text).group(1))
+    assert mib << 20 == bkv.STATIC_SCRATCH_BYTES
 
 
 # ------------------------------------------------------------------------------------------------
@@ -306,3 +308,34 @@ def test_misaligned_pointers_are_rejected():
     d = lib.bkv_decode_attention
     assert d(ctypes.byref(s), arr(FAKE + (4 << 36) + 2), k, v, out, ws, 1 << 40, None) == bkv.BKV_EINVAL
     assert d(ctypes.byref(s), arr(FAKE + (4 << 36)), arr(FAKE + 8), v, out, ws, 1 << 40, None) == bkv.BKV_EINVAL
+
+
+def compress_static_call(s=None, ko=None, k=None, window=32, nb_max=16, budget=64):
+    lib = bkv.load()
+    s = s or shape()
+    return lib.bkv_compress_static(ctypes.byref(s), k or arr(FAKE + (1 << 36)), arr(FAKE + (6 << 36)),
+                                   arr(FAKE + (2 << 36)), window, window, arr(FAKE + (3 << 36)),
+                                   arr(FAKE + (4 << 36)), nb_max, budget, arr(FAKE + (5 << 36)),
+                                   arr(FAKE + (7 << 36)), arr(FAKE + (8 << 36)), ko or arr(FAKE + (9 << 36)),
+                                   arr(FAKE + (10 << 36)), None)
+
+
+def test_compress_static_validates_like_compress():
+    assert compress_static_call(ko=arr(FAKE + (5 << 36) + 64)) == bkv.BKV_EALIAS      # k_out inside scores
+    assert compress_static_call(k=arr(FAKE + (1 << 36) + 8)) == bkv.BKV_EINVAL        # misaligned K
+    assert compress_static_call(s=shape(head_dim=96)) == bkv.BKV_EUNSUPPORTED
+    assert compress_static_call(budget=16) == bkv.BKV_EINVAL                          # window > budget
+
+
+def test_compress_static_refuses_what_its_scratch_cannot_hold():
+    """8192 KV heads x 2 slots x 512 observation rows x 8 bytes = 64 MiB of partials for a
+    single layer of a single sequence: more than the static scratch, and no smaller launch
+    group exists, so the call is refused before anything is enqueued, with the need named."""
+    s = shape(n_layers=1, batch=1, n_q_heads=8192, n_kv_heads=8192, capacity=1024)
+    assert compress_static_call(s=s, window=480, nb_max=32, budget=600) == bkv.BKV_EUNSUPPORTED
+    msg = bkv.load().bkv_last_error().decode()
+    assert "67108864" in msg and str(bkv.STATIC_SCRATCH_BYTES) in msg, msg
+    # half the heads fit in one launch of exactly the scratch's size: that call passes the
+    # checks (and here, with no GPU, fails at the first HIP call instead)
+    s = shape(n_layers=1, batch=1, n_q_heads=4096, n_kv_heads=4096, capacity=1024)
+    assert compress_static_call(s=s, window=480, nb_max=32, budget=600) != bkv.BKV_EUNSUPPORTED
