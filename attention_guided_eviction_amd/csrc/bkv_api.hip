@@ -244,6 +244,19 @@ bkv_status check_compact_args(const bkv_shape* s, const void* const* k, const vo
 
 bkv_status hip_status(hipError_t e) { return e == hipSuccess ? BKV_OK : BKV_EHIP; }
 
+// A launch of nl layers has score_slots() statistics slots per unit; every stats
+// workgroup that meets a unit needs one.  Checked for the largest grid the launcher
+// uses (the bound grows with the grid) under each share weighting it may choose.  (The
+// arithmetic in stats_span_bound shows it always holds; the kernels also turn a unit
+// whose partials did not fit into NaN scores rather than drop them silently.)
+bool slots_cover(const bkv_shape* s, int nl) {
+  const int slots = score_slots(s->capacity, nl, s->n_kv_heads);
+  for (const SplitWeights& w : {kWeightsBalanced, kWeightsDefault, SplitWeights{1, 1, 1, 1}})
+    if (stats_span_bound(s->capacity, nl, s->n_kv_heads, kScoreMaxGrid, w.stats_old, w.stats_new) > slots)
+      return false;
+  return true;
+}
+
 // The score call's launches: groups of at most `layers` layers and `seqs` sequences, in
 // layer-major order, all sharing the partials at `ws_base` (laid out as `ws` says).  A
 // group of sequences b0 .. b0+n-1 is the same call on the arrays' sub-blocks that start at
@@ -267,6 +280,8 @@ bkv_status run_score(const bkv_shape* shape, const void* const* k, const void* c
   a.obs_pad = obs_pad_of(shape, window, nb_max);
   a.scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(shape->head_dim)));
   a.mean = mean;
+  for (int nl : {layers, shape->n_layers % layers})
+    if (nl > 0 && !slots_cover(shape, nl)) return BKV_EUNSUPPORTED;
   const size_t hkv = static_cast<size_t>(shape->n_kv_heads), hq = static_cast<size_t>(shape->n_q_heads);
   const size_t d = static_cast<size_t>(shape->head_dim);
   for (int l0 = 0; l0 < shape->n_layers; l0 += layers) {

@@ -92,6 +92,26 @@ inline int score_slots(int capacity, int n_layers, int n_kv_heads) {
   return tiles < sharing ? tiles : sharing;
 }
 
+// Most stats workgroups that can meet one unit of a launch over n_layers layers, for any
+// sequence lengths: `grid` workgroups, the first half weighing A and the rest B (A >= B;
+// A = B = 1 for equal shares), C = A * (grid / 2) + B * (grid - grid / 2).  Of N tiles,
+// the owner of tile c is the workgroup at cum value x(c) = ceil((c + 1) C / N) - 1, and the
+// workgroup index grows by at most one per B cum values.  A unit's nt tiles come with
+// every other (layer, KV head) of its sequence at the same length, so nt <= N / U
+// (U = n_layers * n_kv_heads); its first and last tiles' cum values then differ by at most
+// ceil((nt - 1) C / N) <= ceil(C / U), their workgroups by at most ceil(C / (U B)).  Never
+// more than the unit's tiles or the grid either.  Since C / B <= kScoreMaxGrid (A + B) /
+// (2 B) at the most skewed weights, this never exceeds score_slots().
+inline int stats_span_bound(int capacity, int n_layers, int n_kv_heads, int grid, int A, int B) {
+  const long long u = static_cast<long long>(n_layers) * n_kv_heads;
+  const long long c = static_cast<long long>(A) * (grid / 2) + static_cast<long long>(B) * (grid - grid / 2);
+  long long span = (c + u * B - 1) / (u * B) + 1;
+  const long long tiles = (capacity + kScoreTile - 1) / kScoreTile;
+  span = span < tiles ? span : tiles;
+  span = span < grid ? span : grid;
+  return static_cast<int>(span);
+}
+
 // ---- select ------------------------------------------------------------------------------
 constexpr int kSelectThreads = 1024;
 

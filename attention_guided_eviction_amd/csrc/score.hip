@@ -464,7 +464,10 @@ __device__ inline float finish_tile(const KeyFrag<D>& kf, const uint8_t* qs, con
 }
 
 // Scores of tiles tile0 .. tile0+ntile-1 of one unit.  Its statistics partials are the
-// n_part slots at pm0/pz0 (stride obs_pad), slot s written by workgroup w0 + s.
+// n_part slots at pm0/pz0 (stride obs_pad), slot s written by workgroup w0 + s.  A unit met
+// by more stats workgroups than it has slots (n_part > a.slots; the host sizes the slots so
+// that no launch gets there) lost the partials past the last slot: its scores are then NaN
+// rather than a softmax over part of the keys.
 template <int D, bool MEAN>
 __device__ void finish_segment(const ScoreArgs& a, const UnitInfo& ui, int tile0, int ntile, const float* pm0,
                                const float* pz0, int n_part, uint8_t* smem) {
@@ -476,15 +479,17 @@ __device__ void finish_segment(const ScoreArgs& a, const UnitInfo& ui, int tile0
   KeyFrag<D> kf;
   load_keys<D>(kp, tile0 * kScoreTile + wave * 64, ui.L, kf);
   stage_queries<D>(a, ui, sm.qs);
+  const bool lost = n_part > a.slots;
+  const int n_kept = lost ? a.slots : n_part;
   // log2-sum-exp2 of every observation row from the unit's partials (the loads of up to
   // 8 slots are issued before any is used; slots of workgroups with no tiles are skipped).
   for (int i = threadIdx.x; i < ui.nqb * 32; i += kThreads) {
     float M = kNegInf, Z = 0.f;
-    for (int s0 = 0; s0 < n_part; s0 += 8) {
+    for (int s0 = 0; s0 < n_kept; s0 += 8) {
       float pm[8], pz[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const bool use = s0 + j < n_part;
+        const bool use = s0 + j < n_kept;
         const size_t o = static_cast<size_t>(s0 + j) * a.obs_pad + i;
         pm[j] = use ? pm0[o] : kNegInf;
         pz[j] = use ? pz0[o] : 0.f;
@@ -493,7 +498,7 @@ __device__ void finish_segment(const ScoreArgs& a, const UnitInfo& ui, int tile0
       for (int j = 0; j < 8; ++j) merge_stats(M, Z, pm[j], pz[j]);
     }
     // -lse2_i / c; padding rows -inf: they never win the max.
-    sm.nlse[i] = (i < ui.n_obs && Z > 0.f) ? -(M + log2f(Z)) / a.scale_log2 : kNegInf;
+    sm.nlse[i] = lost ? __builtin_nanf("") : (i < ui.n_obs && Z > 0.f) ? -(M + log2f(Z)) / a.scale_log2 : kNegInf;
   }
   __syncthreads();
   const int t1 = tile0 + ntile;
@@ -531,13 +536,15 @@ __device__ void finish_segment8(const ScoreArgs& a, const UnitInfo& ui, int tile
   KeyFrag<D> kf;
   if (item < n_items) load_keys<D>(kp, key0 + item * 64, ui.L, kf);
   stage_queries<D, kThreads8>(a, ui, sm.qs);
+  const bool lost = n_part > a.slots;
+  const int n_kept = lost ? a.slots : n_part;
   for (int i = threadIdx.x; i < ui.nqb * 32; i += kThreads8) {
     float M = kNegInf, Z = 0.f;
-    for (int s0 = 0; s0 < n_part; s0 += 8) {
+    for (int s0 = 0; s0 < n_kept; s0 += 8) {
       float pm[8], pz[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const bool use = s0 + j < n_part;
+        const bool use = s0 + j < n_kept;
         const size_t o = static_cast<size_t>(s0 + j) * a.obs_pad + i;
         pm[j] = use ? pm0[o] : kNegInf;
         pz[j] = use ? pz0[o] : 0.f;
@@ -545,7 +552,7 @@ __device__ void finish_segment8(const ScoreArgs& a, const UnitInfo& ui, int tile
 #pragma unroll
       for (int j = 0; j < 8; ++j) merge_stats(M, Z, pm[j], pz[j]);
     }
-    sm.nlse[i] = (i < ui.n_obs && Z > 0.f) ? -(M + log2f(Z)) / a.scale_log2 : kNegInf;
+    sm.nlse[i] = lost ? __builtin_nanf("") : (i < ui.n_obs && Z > 0.f) ? -(M + log2f(Z)) / a.scale_log2 : kNegInf;
   }
   if (threadIdx.x == 0) *next_item = kThreads8 / 64;
   __syncthreads();
@@ -596,8 +603,7 @@ __global__ __launch_bounds__(kThreads8) __attribute__((amdgpu_waves_per_eu(2, 2)
     const int w0 = ss.owner(first);
     const UnitInfo ui = unit_info(a, cur.u);
     const size_t unit_part = static_cast<size_t>(cur.u) * a.slots * a.obs_pad;
-    int n_part = ss.owner(first + cur.nt - 1) - w0 + 1;
-    n_part = n_part < a.slots ? n_part : a.slots;
+    const int n_part = ss.owner(first + cur.nt - 1) - w0 + 1;
     finish_segment8<D, MEAN>(a, ui, cur.tile, n, a.part_m + unit_part, a.part_z + unit_part, n_part, smem);
     c += n;
     if (c >= c1 || !next_unit(a, cur)) break;
@@ -646,10 +652,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
     const UnitInfo ui = unit_info(a, cur.u);
     const size_t unit_part = static_cast<size_t>(cur.u) * a.slots * a.obs_pad;
     if (FINISH) {
-      int n_part = ss.owner(first + cur.nt - 1) - w0 + 1;
-      n_part = n_part < a.slots ? n_part : a.slots;
+      const int n_part = ss.owner(first + cur.nt - 1) - w0 + 1;
       finish_segment<D, MEAN>(a, ui, cur.tile, n, a.part_m + unit_part, a.part_z + unit_part, n_part, smem);
-    } else if (w - w0 < a.slots) {
+    } else if (w - w0 < a.slots) {   // past the slots: no partial (the finish pass gives NaN)
       const size_t o = unit_part + static_cast<size_t>(w - w0) * a.obs_pad;
       stats_segment<D>(a, ui, cur.tile, n, a.part_m + o, a.part_z + o, smem);
     }

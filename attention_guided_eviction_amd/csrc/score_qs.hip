@@ -394,6 +394,8 @@ __device__ inline void qs_stats_body(const ScoreArgs& a, uint8_t* ring) {
     const int n = static_cast<int>(left < cur.nt - cur.tile ? left : cur.nt - cur.tile);
     const int w0 = sp.owner(c - cur.tile);   // slot 0 of the unit's partials
     const UnitInfo ui = unit_info(a, cur.u);
+    // A workgroup past the unit's slots (which the host's sizing rules out) has nowhere to
+    // put its partial; the finish pass then gives the unit NaN scores.
     if (w - w0 < a.slots) {
       const size_t o = (static_cast<size_t>(cur.u) * a.slots + (w - w0)) * a.obs_pad;
       qs_stats_segment<D, BPW, NW>(a, ui, cur.tile, n, a.part_m + o, a.part_z + o, ring);

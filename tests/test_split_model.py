@@ -3,7 +3,9 @@ csrc/score_common.h and of the launcher in csrc/score.hip), checked on random sh
 share is non-empty and contiguous, the owner of a tile is the workgroup whose share holds
 it, and no unit is met by more stats workgroups than the statistics slots the library
 sizes its workspace for (read back through bkv_score_workspace_bytes).  A unit met by more
-would lose a partial.  CPU only."""
+would lose a partial (the kernels then give it NaN scores; the library refuses any launch
+whose closed-form bound, stats_span_bound in csrc/bkv_internal.h, exceeds the slots).  The
+bound is checked here against the exact spans as well.  CPU only."""
 import ctypes
 import random
 
@@ -38,6 +40,13 @@ def stats_split(N, grid, paired, weights):
     weighted = paired and G == grid and G % 2 == 0 and N >= 2 * G
     A, B = weights if weighted else (1, 1)
     return Split(N, G, A, B)
+
+
+def span_bound(capacity, n_layers, n_kv_heads, grid, A, B):
+    """Closed-form most workgroups meeting one unit (stats_span_bound in the library)."""
+    u = n_layers * n_kv_heads
+    c = A * (grid // 2) + B * (grid - grid // 2)
+    return min(-(-c // (u * B)) + 1, -(-capacity // TILE), grid)
 
 
 def library_slots(n_layers, batch, n_kv_heads, capacity, obs_pad):
@@ -83,6 +92,7 @@ def _check_random_shapes(seed):
                     if nt[bb]:
                         span = sp.owner(c + nt[bb] - 1) - sp.owner(c) + 1
                         assert span <= slots, (span, slots, n_layers, batch, hkv, cap, lens, grid)
+                        assert span <= span_bound(cap, n_layers, hkv, grid, sp.A, sp.B) <= slots
                         worst = max(worst, span - slots)
                         c += nt[bb]
         assert c == N
@@ -94,3 +104,36 @@ def test_stats_split_fits_the_slots():
     # some unit is met by exactly as many workgroups as there are slots: one slot fewer in
     # the library's sizing would lose partials on these shapes
     assert worst == 0
+
+
+def _worst_span(n_layers, tiles_per_seq, hkv, grid, weights):
+    N = n_layers * hkv * sum(tiles_per_seq)
+    sp = stats_split(N, grid, True, weights)
+    c, worst = 0, 0
+    for _l in range(n_layers):
+        for nt in tiles_per_seq:
+            for _h in range(hkv):
+                if nt:
+                    worst = max(worst, sp.owner(c + nt - 1) - sp.owner(c) + 1)
+                    c += nt
+    return worst
+
+
+@pytest.mark.parametrize("n_layers,hkv", [(1, 1), (1, 3), (1, 7), (3, 1), (1, 11), (2, 3)])
+def test_few_units_with_long_caches(n_layers, hkv):
+    """Few (layer, KV head) units and caches longer than the slot count (where the tile cap
+    does not help): one short sequence ahead of a long one shifts the long units' start
+    across the shares.  The bound holds, and the sweep comes within one workgroup of it."""
+    u = n_layers * hkv
+    gap = 1 << 30
+    for weights in WEIGHTS.values():
+        for tiles in range(1300, 1460, 7):
+            cap = tiles * TILE
+            slots = library_slots(n_layers, 1, hkv, cap, 256)
+            for pre in (0, 1, 2, 3, 5, 8, 13, 21):
+                lens = ([pre] if pre else []) + [tiles]
+                worst = _worst_span(n_layers, lens, hkv, MAX_GRID, weights)
+                bound = span_bound(cap, n_layers, hkv, MAX_GRID, *weights)
+                assert worst <= bound <= slots, (worst, bound, slots, tiles, pre, weights)
+                gap = min(gap, bound - worst)
+    assert gap <= 1 or u == 1   # a single unit meets at most the grid, below the slots
