@@ -48,8 +48,11 @@ __device__ inline void stage_queries(const ScoreArgs& a, const UnitInfo& ui, uin
   constexpr int kChunks = D / 8;
   constexpr int kBatch = 8;
   const int gw = a.group * a.window;
-  const uint16_t* q = a.q[ui.layer];
-  const uint16_t* bc = a.nb_max > 0 ? a.beacons[ui.layer] : nullptr;
+  // the unit's first recent-query row and first beacon row
+  const uint16_t* q0 = a.window > 0 ? a.q[ui.layer] + ((static_cast<size_t>(ui.b) * a.n_q_heads + ui.h * a.group) *
+                                                       a.q_len + (a.q_len - a.window)) * D : nullptr;
+  const uint16_t* b0 = a.nb_max > 0 ? a.beacons[ui.layer] + (static_cast<size_t>(ui.b) * a.n_kv_heads + ui.h) *
+                                                                a.nb_max * D : nullptr;
   const int total = ui.nqb * 32 * kChunks;
   for (int c0 = threadIdx.x; c0 < total; c0 += kBatch * NT) {
     uint4 v[kBatch];
@@ -60,15 +63,11 @@ __device__ inline void stage_queries(const ScoreArgs& a, const UnitInfo& ui, uin
       const int cc = c - r * kChunks;
       v[j] = make_uint4(0, 0, 0, 0);
       if (c < total) {
-        if (r < gw) {
-          const int hq = ui.h * a.group + r / a.window;
-          const int t = a.q_len - a.window + r % a.window;
+        if (r < gw)   // query head h * G + r / window, its row q_len - window + r % window
           v[j] = *reinterpret_cast<const uint4*>(
-              q + ((static_cast<size_t>(ui.b) * a.n_q_heads + hq) * a.q_len + t) * D + cc * 8);
-        } else if (r < ui.n_obs) {
-          v[j] = *reinterpret_cast<const uint4*>(
-              bc + ((static_cast<size_t>(ui.b) * a.n_kv_heads + ui.h) * a.nb_max + (r - gw)) * D + cc * 8);
-        }
+              q0 + (static_cast<size_t>(r / a.window) * a.q_len + r % a.window) * D + cc * 8);
+        else if (r < ui.n_obs)
+          v[j] = *reinterpret_cast<const uint4*>(b0 + static_cast<size_t>(r - gw) * D + cc * 8);
       }
     }
 #pragma unroll

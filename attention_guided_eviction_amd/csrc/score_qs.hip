@@ -111,17 +111,19 @@ __device__ inline void load_rows(const ScoreArgs& a, const UnitInfo& ui, RowRegs
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int gw = a.group * a.window;
+  // the unit's first recent-query row and first beacon row (uniform across the wave)
+  const uint16_t* q0 = a.window > 0 ? a.q[ui.layer] + ((static_cast<size_t>(ui.b) * a.n_q_heads + ui.h * a.group) *
+                                                       a.q_len + (a.q_len - a.window)) * D : nullptr;
+  const uint16_t* b0 = a.nb_max > 0 ? a.beacons[ui.layer] + (static_cast<size_t>(ui.b) * a.n_kv_heads + ui.h) *
+                                                                a.nb_max * D : nullptr;
 #pragma unroll
   for (int b = 0; b < BPW; ++b) {
     const int r = (wave + NW * b) * 32 + (lane & 31);
     const uint16_t* p = nullptr;
-    if (r < gw) {
-      const int hq = ui.h * a.group + r / a.window;
-      const int t = a.q_len - a.window + r % a.window;
-      p = a.q[ui.layer] + ((static_cast<size_t>(ui.b) * a.n_q_heads + hq) * a.q_len + t) * D;
-    } else if (r < ui.n_obs) {
-      p = a.beacons[ui.layer] + ((static_cast<size_t>(ui.b) * a.n_kv_heads + ui.h) * a.nb_max + (r - gw)) * D;
-    }
+    if (r < gw)   // query head h * G + r / window, its row q_len - window + r % window
+      p = q0 + (static_cast<size_t>(r / a.window) * a.q_len + r % a.window) * D;
+    else if (r < ui.n_obs)
+      p = b0 + static_cast<size_t>(r - gw) * D;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
       bf16x8 v = {};

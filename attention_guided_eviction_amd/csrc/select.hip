@@ -2,7 +2,7 @@
 // (BeaconKV page, Figure 5 (c)).
 //
 // One 1024-thread workgroup per unit.  Thread t holds positions t*EPT .. t*EPT+EPT-1 of
-// the unit's scores in registers as bit patterns (non-negative fp32 order like unsigned
+// the unit's scores (in registers, past 32 of them in LDS) as bit patterns (non-negative fp32 order like unsigned
 // integers).  The k-th largest pattern T among the positions before the window is found
 // by a most-significant-digit-first radix select: four passes over 8-bit digits, each an
 // LDS histogram of the candidates that still match the digits chosen so far (built in 16
@@ -77,8 +77,79 @@ __device__ inline void pick_digit(int* hist, int r, int* out) {
   *reinterpret_cast<int4*>(hist + 4 * lane) = make_int4(0, 0, 0, 0);
 }
 
+// Scores a thread keeps in registers; past 32 (capacities above 32768) the rest sit in
+// LDS, element i of thread t at word (i - 32) * kSelectThreads + t, so that the registers
+// of 16 waves per CU stay within the register file without spilling.
+template <int EPT>
+struct Held {
+  static constexpr int kReg = EPT > 32 ? 32 : EPT;
+  static constexpr int kLds = EPT - kReg;
+  uint32_t r[kReg];
+  uint32_t* lds;
+  __device__ uint32_t& at_lds(int i) const { return lds[(i - kReg) * kSelectThreads + threadIdx.x]; }
+};
+
+// Per element (in position order: the register part unrolled, the LDS part as a loop):
+// add a candidate matching the digits chosen so far to the histogram of the next digit,
+struct HistStep {
+  int prefix, pass, shift;
+  uint32_t P;
+  int* copy;
+  __device__ void operator()(int j, uint32_t xi) const {
+    if (j < prefix && (pass == 0 || (xi >> (shift + 8)) == P)) atomicAdd(&copy[(xi >> shift) & 255u], 1);
+  }
+};
+
+// count positions kept outright (candidates above T, the window) and ties at T,
+struct CountStep {
+  int prefix, L, want;
+  uint32_t T;
+  int n_fixed = 0, n_eq = 0;
+  __device__ void operator()(int j, uint32_t xi) {
+    const bool cand = j < prefix;
+    n_fixed += (cand ? want > 0 && xi > T : j < L) ? 1 : 0;
+    n_eq += (cand && want > 0 && xi == T) ? 1 : 0;
+  }
+};
+
+// and write the kept positions (ties at T: the first need_eq of them).
+struct WriteStep {
+  int prefix, L, want, need_eq, budget;
+  uint32_t T;
+  int eq_seen, pos;
+  int32_t* out;
+  __device__ void operator()(int j, uint32_t xi) {
+    bool keep;
+    if (j < prefix) {
+      keep = want > 0 && xi > T;
+      if (want > 0 && xi == T) {
+        keep = eq_seen < need_eq;
+        ++eq_seen;
+      }
+    } else {
+      keep = j < L;
+    }
+    if (keep) {
+      if (pos < budget) out[pos] = j;
+      ++pos;
+    }
+  }
+};
+
+template <int EPT, class Step>
+__device__ inline void for_each_held(const Held<EPT>& x, int j0, Step& step) {
+#pragma unroll
+  for (int i = 0; i < Held<EPT>::kReg; ++i) step(j0 + i, x.r[i]);
+#pragma unroll 4
+  for (int i = Held<EPT>::kReg; i < EPT; ++i) step(j0 + i, x.at_lds(i));
+}
+
+// Orders -0 as 0 (the other patterns of non-negative fp32 values order as unsigned ints).
+__device__ inline uint32_t pattern(uint32_t u) { return u == 0x80000000u ? 0u : u; }
+
 template <int EPT>
 __global__ __launch_bounds__(kSelectThreads) void select_topk_kernel(const SelectArgs a) {
+  __shared__ uint32_t held_lds[Held<EPT>::kLds > 0 ? Held<EPT>::kLds * kSelectThreads : 1];
   __shared__ __attribute__((aligned(16))) int hist[256];
   __shared__ int histc[kCopies * kCopyStride];
   __shared__ unsigned long long scan_buf[kWaves];
@@ -103,22 +174,32 @@ __global__ __launch_bounds__(kSelectThreads) void select_topk_kernel(const Selec
   const float* sc = a.scores[layer] + static_cast<size_t>(bh) * a.capacity;
   const int j0 = tid * EPT;
 
-  uint32_t x[EPT];
+  Held<EPT> x;
+  x.lds = held_lds;
+  constexpr int kReg = Held<EPT>::kReg;
   if (EPT % 4 == 0 && (reinterpret_cast<uintptr_t>(sc) & 15) == 0 && j0 + EPT <= prefix) {
 #pragma unroll
-    for (int i = 0; i < EPT; i += 4) {
+    for (int i = 0; i < kReg; i += 4) {
       const uint4 v = *reinterpret_cast<const uint4*>(sc + j0 + i);
-      x[i] = v.x;
-      x[i + 1] = v.y;
-      x[i + 2] = v.z;
-      x[i + 3] = v.w;
+      x.r[i] = pattern(v.x);
+      x.r[i + 1] = pattern(v.y);
+      x.r[i + 2] = pattern(v.z);
+      x.r[i + 3] = pattern(v.w);
+    }
+#pragma unroll 2
+    for (int i = kReg; i < EPT; i += 4) {
+      const uint4 v = *reinterpret_cast<const uint4*>(sc + j0 + i);
+      x.at_lds(i) = pattern(v.x);
+      x.at_lds(i + 1) = pattern(v.y);
+      x.at_lds(i + 2) = pattern(v.z);
+      x.at_lds(i + 3) = pattern(v.w);
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < EPT; ++i) x[i] = j0 + i < prefix ? __float_as_uint(sc[j0 + i]) : 0u;
+    for (int i = 0; i < kReg; ++i) x.r[i] = j0 + i < prefix ? pattern(__float_as_uint(sc[j0 + i])) : 0u;
+#pragma unroll 4
+    for (int i = kReg; i < EPT; ++i) x.at_lds(i) = j0 + i < prefix ? pattern(__float_as_uint(sc[j0 + i])) : 0u;
   }
-#pragma unroll
-  for (int i = 0; i < EPT; ++i) x[i] = x[i] == 0x80000000u ? 0u : x[i];   // -0 orders as 0
 
   // Radix select of the want-th largest pattern among the candidates.
   uint32_t T = 0;
@@ -133,11 +214,8 @@ __global__ __launch_bounds__(kSelectThreads) void select_topk_kernel(const Selec
 #pragma unroll
     for (int pass = 0; pass < 4; ++pass) {
       const int shift = 24 - 8 * pass;
-#pragma unroll
-      for (int i = 0; i < EPT; ++i) {
-        const bool match = j0 + i < prefix && (pass == 0 || (x[i] >> (shift + 8)) == P);
-        if (match) atomicAdd(&my_copy[(x[i] >> shift) & 255u], 1);
-      }
+      HistStep step{prefix, pass, shift, P, my_copy};
+      for_each_held(x, j0, step);
       __syncthreads();
       if (tid < 256) {   // fold the copies (and clear them for the next pass)
         int sum = 0;
@@ -160,42 +238,16 @@ __global__ __launch_bounds__(kSelectThreads) void select_topk_kernel(const Selec
 
   // Per-thread counts in position order: ties at T, and positions kept outright
   // (candidates above T, and the window).
-  int n_eq = 0, n_fixed = 0;
-#pragma unroll
-  for (int i = 0; i < EPT; ++i) {
-    const int j = j0 + i;
-    if (j < prefix) {
-      if (want > 0) {
-        n_fixed += x[i] > T ? 1 : 0;
-        n_eq += x[i] == T ? 1 : 0;
-      }
-    } else if (j < L) {
-      ++n_fixed;
-    }
-  }
+  CountStep count{prefix, L, want, T};
+  for_each_held(x, j0, count);
+  const int n_eq = count.n_eq, n_fixed = count.n_fixed;
   const unsigned long long before =
       block_exclusive_scan((static_cast<unsigned long long>(n_eq) << 32) | static_cast<unsigned>(n_fixed), scan_buf);
-  int eq_seen = static_cast<int>(before >> 32);
+  const int eq_before = static_cast<int>(before >> 32);
   const int fixed_before = static_cast<int>(before & 0xffffffffu);
-  int pos = fixed_before + (eq_seen < need_eq ? eq_seen : need_eq);
-#pragma unroll
-  for (int i = 0; i < EPT; ++i) {
-    const int j = j0 + i;
-    bool keep;
-    if (j < prefix) {
-      keep = want > 0 && x[i] > T;
-      if (want > 0 && x[i] == T) {
-        keep = eq_seen < need_eq;
-        ++eq_seen;
-      }
-    } else {
-      keep = j < L;
-    }
-    if (keep) {
-      if (pos < a.budget) out[pos] = j;
-      ++pos;
-    }
-  }
+  WriteStep write{prefix, L, want, need_eq, a.budget, T, eq_before,
+                  fixed_before + (eq_before < need_eq ? eq_before : need_eq), out};
+  for_each_held(x, j0, write);
   if (tid == 0) a.n_kept[layer][bh] = a.budget;
 }
 

@@ -19,6 +19,7 @@ import argparse
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -32,8 +33,10 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=3)
+    # Enough untimed steps that the GPU has reached its working clocks before the timed
+    # ones (a cold start under-reports short events by about a tenth).
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--workload", default="qwen7b_16k")
     p.add_argument("--cpu-units", type=int, default=-1,
                    help="at most this many units in the CPU-oracle sample (0: skip; -1: no limit; "
@@ -115,18 +118,37 @@ def copy_ceiling(dev, gib=2, reps=5):
     return 2 * gib * (1 << 30) / (statistics.median(times) * 1e-3) / 1e9
 
 
+def _profile_values(path):
+    """key = value lines of a committed profile summary (comment lines skipped)."""
+    vals = {}
+    if not os.path.exists(path):
+        return vals
+    with open(path) as f:
+        for line in f:
+            m = re.match(r"\s*([a-z_0-9]+) = (\S+)\s*$", line)
+            if m:
+                vals[m.group(1)] = m.group(2)
+    return vals
+
+
+def score_counters(workload):
+    """MFMA / VALU busy fractions of the scorer's two passes from the committed counter
+    summary for this workload, or None when there is none or the scorer source has changed
+    since the counters were taken."""
+    vals = _profile_values(os.path.join(ROOT, "profiles", f"score_counters_{workload}.md"))
+    if vals.get("scorer_sha256") != scorer_digest():
+        return None
+    keys = ("mfma_busy_stats", "mfma_busy_finish", "valu_busy_stats", "valu_busy_finish", "coexec_stats",
+            "coexec_finish")
+    if not all(k in vals for k in keys):
+        return None
+    return {k: float(vals[k]) for k in keys} | {"source": f"profiles/score_counters_{workload}.md"}
+
+
 def score_traffic(workload):
     """HBM bytes per bkv_score call from the committed counter summary for this workload,
     or None when there is none or the scorer source has changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"score_traffic_{workload}.txt")
-    if not os.path.exists(path):
-        return None
-    vals = {}
-    with open(path) as f:
-        for line in f:
-            if "=" in line and not line.lstrip().startswith("#"):
-                k, v = line.split("=", 1)
-                vals[k.strip()] = v.strip()
+    vals = _profile_values(os.path.join(ROOT, "profiles", f"score_traffic_{workload}.txt"))
     if vals.get("scorer_sha256") != scorer_digest() or "traffic_bytes_per_call" not in vals:
         return None
     return float(vals["traffic_bytes_per_call"])
@@ -229,8 +251,9 @@ class CpuBaseline:
                 "single_process_s_per_unit": round(per_unit, 4),
                 "single_process_s_all_units": round(per_unit * w.units, 1),
                 "sample": f"{done} of {w.units} (layer, sequence, KV head) units of {w.name} in seeded random order, "
-                          f"{len(shares)} processes x up to {k} units (~{budget_s:.0f} s each, one BLAS thread per "
-                          f"process), {rows} cached rows in {wall:.1f} s wall; float64 NumPy beacon update, scores, "
+                          f"{len(shares)} processes x up to {k} units (at most ~{budget_s:.0f} s of oracle work each, "
+                          f"one BLAS thread per process), {rows} cached rows in {wall:.2f} s wall; float64 NumPy beacon "
+                          f"update, scores, "
                           f"top-K and compaction; inputs built before the timed region; rows/s divided by "
                           f"layers x KV heads"}
 
@@ -453,6 +476,9 @@ def main():
         "per_call_gbs": {n: {"alg_bytes": ab[n], "achieved": round(ab[n] / (t * 1e-3) / 1e9, 1),
                              "frac": round(ab[n] / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)} for n, t in per.items()},
         "roofline": roof,
+        # utilisation of the scorer's passes from the committed counter summary (same scorer
+        # sources and workload only)
+        "mfma_busy": score_counters(w.name) if dom == "score" and as_named else None,
     }
     # Same-run ceiling: a plain read+write device copy of 4 GiB moved.
     ceil = copy_ceiling(dev)
