@@ -7,14 +7,14 @@
 // row (the workgroup is the largest pool rounded up to whole waves, so two units share a CU
 // on the largest workloads); larger pools take fps_pool_kernel below.  Thread p
 // holds pool row p (live beacons, then the group's new queries head-major in time order)
-// in registers as packed bf16 pairs, with its inverse norm.  The pick's owner copies its
-// row into LDS; after a barrier every wave reads it there (one address: a broadcast) into
-// scalar registers, and each thread takes the dot product of its row with it by
-// v_dot2_f32_bf16 with the row in SGPRs: no cross-lane reduction per row.  Each thread
-// keeps its row's distance to the nearest chosen row; a block-wide max of (distance,
-// lowest index on ties) names the next pick: a DPP max per wave, then one 64-bit LDS atomic
-// max per wave of (distance key, complement of the index), read back by every thread after
-// a barrier.  Two barriers per pick.
+// in registers as packed bf16 pairs, with its inverse norm.  Once a pick is known every
+// wave loads its row from the (read-only) pool source into scalar registers by scalar
+// loads, and each thread takes the dot product of its row with it by v_dot2_f32_bf16 with
+// the row in SGPRs: no cross-lane reduction and no per-word lane moves.  Each thread keeps
+// its row's distance to the nearest chosen row; a block-wide max of (distance, lowest index
+// on ties) names the next pick: a DPP max per wave, then one 64-bit LDS atomic max per wave
+// of (distance key, complement of the index), read back by every thread after a barrier.
+// One barrier per pick.
 
 #include "bkv_internal.h"
 
@@ -25,6 +25,8 @@ constexpr int kWaves = kFpsThreads / 64;
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef const __attribute__((address_space(4))) uint32_t* const_u32;
+typedef __attribute__((ext_vector_type(16))) uint32_t u32x16;
+typedef const __attribute__((address_space(4))) u32x16* const_u32x16;
 
 __device__ inline float dot2(uint32_t x, uint32_t y, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), __builtin_bit_cast(bf16x2, y), acc, false);
@@ -47,8 +49,8 @@ template <int D>
 __global__ __launch_bounds__(kFpsThreads) void fps_kernel(const FpsArgs a) {
   constexpr int W = D / 2;   // 32-bit words (bf16 pairs) per row
   __shared__ float inv_s[kFpsThreads];
+  __shared__ unsigned long long src_s[kFpsThreads];   // address of each pool row's source
   __shared__ unsigned long long best[3];   // per pick (mod 3): max of (distance key << 32 | ~index)
-  __shared__ uint4 pick_row[W / 4];        // the pick's row, written by its owner
   const int nthr = static_cast<int>(blockDim.x);
 
   const int u = blockIdx.x;
@@ -90,6 +92,7 @@ __global__ __launch_bounds__(kFpsThreads) void fps_kernel(const FpsArgs a) {
   uint32_t x[W];
   if (have) {
     const uint4* src = reinterpret_cast<const uint4*>(row_ptr(p));
+    src_s[p] = reinterpret_cast<unsigned long long>(src);
 #pragma unroll
     for (int i = 0; i < W / 4; ++i) {
       const uint4 v = src[i];
@@ -117,27 +120,29 @@ __global__ __launch_bounds__(kFpsThreads) void fps_kernel(const FpsArgs a) {
     if (p == cur) {   // the pick's owner writes it out and leaves the candidates
       uint4* dst = reinterpret_cast<uint4*>(out + static_cast<size_t>(t) * D);
 #pragma unroll
-      for (int i = 0; i < W / 4; ++i) {
-        const uint4 v = make_uint4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
-        dst[i] = v;
-        pick_row[i] = v;
-      }
+      for (int i = 0; i < W / 4; ++i) dst[i] = make_uint4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
       avail = false;
     }
     if (t == a.nb_max - 1) break;
-    __syncthreads();   // the pick's row is in LDS
     unsigned key = 0;   // distance bits + 1 (monotone for distances >= 0); 0: cannot be picked
     if ((tid & ~63) < P) {   // waves holding no pool row skip the products
-      float acc[4] = {0.f, 0.f, 0.f, 0.f};   // four chains: shorter dependency
+      // the pick's row from its read-only source, through the scalar cache: its address is
+      // one LDS word for the whole block, moved to scalar registers
+      const unsigned long long sa = src_s[cur];
+      const unsigned lo = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(sa));
+      const unsigned hi = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(sa >> 32));
+      const const_u32x16 y = (const_u32x16)((static_cast<unsigned long long>(hi) << 32) | lo);
+      // all of the row's loads issued before the first product: one scalar-cache round trip
+      u32x16 yr[W / 16];
 #pragma unroll
-      for (int i = 0; i < W / 4; ++i) {
-        const uint4 v = pick_row[i];   // one address for the wave: a broadcast
-        acc[0] = dot2(x[4 * i], __builtin_amdgcn_readfirstlane(v.x), acc[0]);
-        acc[1] = dot2(x[4 * i + 1], __builtin_amdgcn_readfirstlane(v.y), acc[1]);
-        acc[2] = dot2(x[4 * i + 2], __builtin_amdgcn_readfirstlane(v.z), acc[2]);
-        acc[3] = dot2(x[4 * i + 3], __builtin_amdgcn_readfirstlane(v.w), acc[3]);
+      for (int i = 0; i < W / 16; ++i) yr[i] = y[i];
+      float acc[2] = {0.f, 0.f};   // two chains: shorter dependency
+#pragma unroll
+      for (int i = 0; i < W / 2; ++i) {
+        acc[0] = dot2(x[2 * i], yr[i / 8][(2 * i) % 16], acc[0]);
+        acc[1] = dot2(x[2 * i + 1], yr[i / 8][(2 * i + 1) % 16], acc[1]);
       }
-      const float dt = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+      const float dt = acc[0] + acc[1];
       float d = 1.0f - dt * inv * inv_s[cur];
       d = fminf(fmaxf(d, 0.f), 2.f);
       mind = t == 0 ? d : fminf(mind, d);
@@ -147,7 +152,9 @@ __global__ __launch_bounds__(kFpsThreads) void fps_kernel(const FpsArgs a) {
     // lowest lane holding the wave max = lowest pool index of the wave; one LDS max per
     // wave of (key, complement of the index): the largest key wins, then the lowest index
     const unsigned long long hit = __ballot(key == wmax);
-    if (tid == 0) best[(t + 1) % 3] = 0ull;   // last read before the previous pick's barrier
+    // best[(t + 1) % 3] was last read right after pick t - 2's barrier, which every thread
+    // has left behind since passing pick t - 1's barrier: safe to clear for pick t + 1
+    if (tid == 0) best[(t + 1) % 3] = 0ull;
     if ((tid & 63) == 0) {
       const unsigned idx = static_cast<unsigned>((tid & ~63) + __ffsll(static_cast<long long>(hit)) - 1);
       atomicMax(&best[t % 3], (static_cast<unsigned long long>(wmax) << 32) | (0xffffffffu - idx));
