@@ -89,61 +89,6 @@ struct Held {
   __device__ uint32_t& at_lds(int i) const { return lds[(i - kReg) * kSelectThreads + threadIdx.x]; }
 };
 
-// Per element (in position order: the register part unrolled, the LDS part as a loop):
-// add a candidate matching the digits chosen so far to the histogram of the next digit,
-struct HistStep {
-  int prefix, pass, shift;
-  uint32_t P;
-  int* copy;
-  __device__ void operator()(int j, uint32_t xi) const {
-    if (j < prefix && (pass == 0 || (xi >> (shift + 8)) == P)) atomicAdd(&copy[(xi >> shift) & 255u], 1);
-  }
-};
-
-// count positions kept outright (candidates above T, the window) and ties at T,
-struct CountStep {
-  int prefix, L, want;
-  uint32_t T;
-  int n_fixed = 0, n_eq = 0;
-  __device__ void operator()(int j, uint32_t xi) {
-    const bool cand = j < prefix;
-    n_fixed += (cand ? want > 0 && xi > T : j < L) ? 1 : 0;
-    n_eq += (cand && want > 0 && xi == T) ? 1 : 0;
-  }
-};
-
-// and write the kept positions (ties at T: the first need_eq of them).
-struct WriteStep {
-  int prefix, L, want, need_eq, budget;
-  uint32_t T;
-  int eq_seen, pos;
-  int32_t* out;
-  __device__ void operator()(int j, uint32_t xi) {
-    bool keep;
-    if (j < prefix) {
-      keep = want > 0 && xi > T;
-      if (want > 0 && xi == T) {
-        keep = eq_seen < need_eq;
-        ++eq_seen;
-      }
-    } else {
-      keep = j < L;
-    }
-    if (keep) {
-      if (pos < budget) out[pos] = j;
-      ++pos;
-    }
-  }
-};
-
-template <int EPT, class Step>
-__device__ inline void for_each_held(const Held<EPT>& x, int j0, Step& step) {
-#pragma unroll
-  for (int i = 0; i < Held<EPT>::kReg; ++i) step(j0 + i, x.r[i]);
-#pragma unroll 4
-  for (int i = Held<EPT>::kReg; i < EPT; ++i) step(j0 + i, x.at_lds(i));
-}
-
 // Orders -0 as 0 (the other patterns of non-negative fp32 values order as unsigned ints).
 __device__ inline uint32_t pattern(uint32_t u) { return u == 0x80000000u ? 0u : u; }
 
@@ -195,10 +140,22 @@ __global__ __launch_bounds__(kSelectThreads) void select_topk_kernel(const Selec
       x.at_lds(i + 3) = pattern(v.w);
     }
   } else {
+    // Unconditional loads at clamped positions (prefix >= 1 here: L > budget >= window), so
+    // that all of a thread's loads are in flight together; positions past the candidates
+    // then read as 0.  A branch per element would wait for each load in turn, and the
+    // thread at the candidates' end would hold up the whole workgroup at the next barrier.
 #pragma unroll
-    for (int i = 0; i < kReg; ++i) x.r[i] = j0 + i < prefix ? pattern(__float_as_uint(sc[j0 + i])) : 0u;
+    for (int i = 0; i < kReg; ++i) {
+      const int j = j0 + i;
+      const uint32_t v = __float_as_uint(sc[j < prefix ? j : prefix - 1]);
+      x.r[i] = j < prefix ? pattern(v) : 0u;
+    }
 #pragma unroll 4
-    for (int i = kReg; i < EPT; ++i) x.at_lds(i) = j0 + i < prefix ? pattern(__float_as_uint(sc[j0 + i])) : 0u;
+    for (int i = kReg; i < EPT; ++i) {
+      const int j = j0 + i;
+      const uint32_t v = __float_as_uint(sc[j < prefix ? j : prefix - 1]);
+      x.at_lds(i) = j < prefix ? pattern(v) : 0u;
+    }
   }
 
   // Radix select of the want-th largest pattern among the candidates.
@@ -214,8 +171,16 @@ __global__ __launch_bounds__(kSelectThreads) void select_topk_kernel(const Selec
 #pragma unroll
     for (int pass = 0; pass < 4; ++pass) {
       const int shift = 24 - 8 * pass;
-      HistStep step{prefix, pass, shift, P, my_copy};
-      for_each_held(x, j0, step);
+#pragma unroll
+      for (int i = 0; i < kReg; ++i) {
+        const uint32_t xi = x.r[i];
+        if (j0 + i < prefix && (pass == 0 || (xi >> (shift + 8)) == P)) atomicAdd(&my_copy[(xi >> shift) & 255u], 1);
+      }
+#pragma unroll 4
+      for (int i = kReg; i < EPT; ++i) {
+        const uint32_t xi = x.at_lds(i);
+        if (j0 + i < prefix && (pass == 0 || (xi >> (shift + 8)) == P)) atomicAdd(&my_copy[(xi >> shift) & 255u], 1);
+      }
       __syncthreads();
       if (tid < 256) {   // fold the copies (and clear them for the next pass)
         int sum = 0;
@@ -238,16 +203,42 @@ __global__ __launch_bounds__(kSelectThreads) void select_topk_kernel(const Selec
 
   // Per-thread counts in position order: ties at T, and positions kept outright
   // (candidates above T, and the window).
-  CountStep count{prefix, L, want, T};
-  for_each_held(x, j0, count);
-  const int n_eq = count.n_eq, n_fixed = count.n_fixed;
+  int n_eq = 0, n_fixed = 0;
+  auto count = [&](int j, uint32_t xi) {
+    const bool cand = j < prefix;
+    n_fixed += (cand ? want > 0 && xi > T : j < L) ? 1 : 0;
+    n_eq += (cand && want > 0 && xi == T) ? 1 : 0;
+  };
+#pragma unroll
+  for (int i = 0; i < kReg; ++i) count(j0 + i, x.r[i]);
+#pragma unroll 4
+  for (int i = kReg; i < EPT; ++i) count(j0 + i, x.at_lds(i));
   const unsigned long long before =
       block_exclusive_scan((static_cast<unsigned long long>(n_eq) << 32) | static_cast<unsigned>(n_fixed), scan_buf);
   const int eq_before = static_cast<int>(before >> 32);
   const int fixed_before = static_cast<int>(before & 0xffffffffu);
-  WriteStep write{prefix, L, want, need_eq, a.budget, T, eq_before,
-                  fixed_before + (eq_before < need_eq ? eq_before : need_eq), out};
-  for_each_held(x, j0, write);
+  int eq_seen = eq_before;
+  int pos = fixed_before + (eq_before < need_eq ? eq_before : need_eq);
+  auto write = [&](int j, uint32_t xi) {
+    bool keep;
+    if (j < prefix) {
+      keep = want > 0 && xi > T;
+      if (want > 0 && xi == T) {
+        keep = eq_seen < need_eq;
+        ++eq_seen;
+      }
+    } else {
+      keep = j < L;
+    }
+    if (keep) {
+      if (pos < a.budget) out[pos] = j;
+      ++pos;
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < kReg; ++i) write(j0 + i, x.r[i]);
+#pragma unroll 4
+  for (int i = kReg; i < EPT; ++i) write(j0 + i, x.at_lds(i));
   if (tid == 0) a.n_kept[layer][bh] = a.budget;
 }
 
