@@ -17,7 +17,10 @@ import numpy as np
 import pytest
 import torch
 
-from parity import build_inputs, check_selection, log
+import gc
+from types import SimpleNamespace
+
+from parity import build_inputs, check_selection, check_units, log, sample_units
 from synth import WORKLOADS
 from attention_guided_eviction_amd import bkv
 
@@ -140,3 +143,23 @@ def test_static_repeats_bit_identically_after_a_larger_call():
     _prepare(tiny, tin, ref, False)()
     torch.cuda.synchronize()
     _assert_identical(tiny, ref, again)
+
+
+def test_static_full_serving_shape_against_the_oracle():
+    """The Qwen3-4B serving shape at full size (36 layers, batch 64 ragged 2048-8192, 135 MiB
+    of partials by default): the static call scores it in launch groups that fit the
+    scratch; sampled units checked against the oracle one by one."""
+    w = WORKLOADS["qwen4b_serving"].replace(name="static_serving", t_new=0)
+    inp = build_inputs(w)
+    need = bkv.compress_workspace_bytes(_shape(w, inp), w.window, w.nb_max, w.budget)
+    assert need > bkv.STATIC_SCRATCH_BYTES, need
+    out = _outputs(w)
+    log(f"[static] {w.name}: default partials {need / 2**20:.0f} MiB; one static call")
+    _prepare(w, inp, out, True)()
+    torch.cuda.synchronize()
+    ev = SimpleNamespace(cfg=SimpleNamespace(aggregation="max"), **out)
+    worst = check_units(w, ev, sample_units(w, 6, seed=5), inp)
+    log(f"[static] {w.name}: worst {worst}")
+    del inp, out, ev
+    gc.collect()
+    torch.cuda.empty_cache()
