@@ -319,15 +319,18 @@ bkv_status bkv_compress(const bkv_shape* shape,
 /* ------------------------------------------------------------------------------------
  * For callers that cannot allocate device memory (code under HIP graph capture, tight
  * serving loops, harnesses that forbid hipMalloc): bkv_compress without a workspace
- * argument.  Same arguments otherwise, same results, same errors (no BKV_EWORKSPACE).
+ * argument.  Same arguments otherwise, same errors (no BKV_EWORKSPACE), and bit-identical
+ * results wherever the default launches' partials fit the scratch.
  *
  * The score stage's statistics partials go to a static device array of
  * BKV_STATIC_SCRATCH_BYTES bytes that the library's code object holds on every device it
  * is loaded on, until the process ends; the call itself allocates and frees nothing.
  * Where the default launches' partials would not fit, the score stage goes out in groups
- * of fewer layers and sequences per launch (same results, more launches).  If even one
- * layer of one sequence does not fit the call returns BKV_EUNSUPPORTED and enqueues
- * nothing; bkv_last_error() then says how many bytes it would need.
+ * of fewer layers and sequences per launch (more launches; the scores may then differ from
+ * bkv_compress's in the last bits, since the keys are summed in pieces that follow the
+ * launch size, and a top-K can flip at such a near-tie).  If even one layer of one
+ * sequence does not fit, the call returns BKV_EUNSUPPORTED and enqueues nothing;
+ * bkv_last_error() then says how many bytes it would need.
  *
  * Every call on one device shares that device's array, and each call's partials are
  * written before they are read in the same call, so nothing needs clearing between calls.
