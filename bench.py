@@ -79,6 +79,25 @@ def alg_bytes(w, lens):
     return {"score": score, "select": select, "compact": compact, "update_beacons": fps}
 
 
+def event_bytes(w, lens):
+    """Algorithmic HBM bytes of one whole event: K read once, the observation rows, the kept
+    K/V rows read and written, the kept positions once, and (with a beacon update) the pool
+    read and the beacons written.  The score vector written by the scorer and read back by
+    the selection is traffic of splitting the event into stages, not of the method, and is
+    not counted (the per-stage figures above do count it)."""
+    D, G = w.head_dim, w.group
+    n_obs = G * w.window + w.nb_max
+    total = 0
+    for L in lens:
+        L = int(L)
+        N = min(w.budget, L)
+        u = w.n_layers * w.n_kv_heads
+        total += u * (L * D * 2 + n_obs * D * 2 + 4 * N * D * 2 + N * 4)
+        if w.runs_fps:
+            total += u * ((w.nb_init + G * w.t_new) * D * 2 + w.nb_max * D * 2)
+    return total
+
+
 def score_flops(w, lens):
     n_obs = w.group * w.window + w.nb_max
     return sum(2.0 * n_obs * int(L) * w.head_dim * w.n_layers * w.n_kv_heads for L in lens)
@@ -436,7 +455,7 @@ def main():
 
     tokens = float(lens.sum())
     ab = alg_bytes(w, lens)
-    total_bytes = sum(ab.values())
+    total_bytes = event_bytes(w, lens)
     dom = max(per, key=per.get)
     achieved = ab[dom] / (per[dom] * 1e-3) / 1e9
     # The committed counter summary holds for the workload as named, max aggregation.
