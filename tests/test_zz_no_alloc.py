@@ -163,3 +163,18 @@ def test_static_full_serving_shape_against_the_oracle():
     del inp, out, ev
     gc.collect()
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_static_random_geometries_bit_identical(seed):
+    """Random small geometries (those of the random parity cases, without the beacon
+    update): the default grouping fits the scratch, so every output is bit-identical to
+    bkv_compress's."""
+    from test_parity_random_gpu import _workload
+    w = _workload(seed)[0].replace(t_new=0)
+    inp = build_inputs(w)
+    ref, got = _outputs(w), _outputs(w)
+    _prepare(w, inp, ref, False)()
+    _prepare(w, inp, got, True)()
+    torch.cuda.synchronize()
+    _assert_identical(w, ref, got)
