@@ -178,3 +178,25 @@ def test_static_random_geometries_bit_identical(seed):
     _prepare(w, inp, got, True)()
     torch.cuda.synchronize()
     _assert_identical(w, ref, got)
+
+
+def test_static_grouped_with_an_empty_sequence_group_and_many_layers():
+    """Edge cases of the launch grouping: the grouped shape with its first three sequences
+    empty (the first sequence group has no keys at all), and a 50-layer model (a layer
+    group of 48 and one of 2).  Compared with bkv_compress as in the grouped case."""
+    w = GROUPED.replace(name="static_empty_group", ragged=None, seq_len=None, lengths=(0, 0, 0, 3072, 2000, 999))
+    inp = build_inputs(w)
+    assert bkv.compress_workspace_bytes(_shape(w, inp), w.window, w.nb_max, w.budget) > bkv.STATIC_SCRATCH_BYTES
+    ref, got = _outputs(w), _outputs(w)
+    _prepare(w, inp, ref, False)()
+    _prepare(w, inp, got, True)()
+    torch.cuda.synchronize()
+    _assert_equivalent(w, inp, ref, got)
+    many = WORKLOADS["tiny"].replace(name="static_many_layers", n_layers=50, capacity=256, seq_len=250, budget=64,
+                                     t_new=0)
+    inp = build_inputs(many)
+    ref, got = _outputs(many), _outputs(many)
+    _prepare(many, inp, ref, False)()
+    _prepare(many, inp, got, True)()
+    torch.cuda.synchronize()
+    _assert_identical(many, ref, got)
