@@ -59,6 +59,26 @@ def parse():
     return p.parse_args()
 
 
+def score_kernel_names(head_dim: int, n_obs: int) -> tuple:
+    """The two kernels one bkv_score call launches for this geometry, by the library's own
+    dispatch rules: the register-row stats pass up to 256 padded observation rows (4 waves),
+    8 waves up to 512 at head_dim 128, 3 blocks per wave up to 384 at head_dim 64, else the
+    LDS-staged stats pass; the 4-wave finish where two workgroups' staged rows and
+    statistics fit in one CU's 160 KiB of LDS, else the 8-wave finish."""
+    obs_pad = -(-n_obs // 32) * 32
+    if obs_pad <= 256:
+        stats = "qs_stats_kernel<D,BPW>"
+    elif head_dim == 128 and obs_pad <= 512:
+        stats = "qs_stats_kernel8<D>"
+    elif head_dim == 64 and obs_pad <= 384:
+        stats = "qs_stats_kernel_wide<D,3>"
+    else:
+        stats = "score_kernel<D,false>"
+    lds = obs_pad * head_dim * 2 + 4 * 4 * obs_pad * 4
+    finish = "score_kernel<D,true>" if 2 * lds <= 160 * 1024 else "finish8_kernel<D>"
+    return stats, finish
+
+
 def alg_bytes(w, lens):
     """Algorithmic HBM bytes of one event per kernel group: K rows read once and the
     observation queries (score), scores read and positions written (select), kept K/V rows
@@ -461,10 +481,8 @@ def main():
     # The committed counter summary holds for the workload as named, max aggregation.
     as_named = args.window is None and args.beacons is None and args.budget is None and args.aggregation == "max"
     traffic = score_traffic(w.name) if dom == "score" and as_named else None
-    obs_pad = -(-(w.group * w.window + w.nb_max) // 32) * 32
-    stats_kernel = ("qs_stats_kernel<D,BPW>" if obs_pad <= 256 else
-                    "qs_stats_kernel_wide<D,3>" if obs_pad <= 384 else "score_kernel<D,false>")
-    roof = {"kernel": {"score": f"{stats_kernel} (stats) + score_kernel<D,true> (finish): one bkv_score call",
+    stats_kernel, finish_kernel = score_kernel_names(w.head_dim, w.group * w.window + w.nb_max)
+    roof = {"kernel": {"score": f"{stats_kernel} (stats) + {finish_kernel} (finish): one bkv_score call",
                        "select": "select_topk_kernel (bkv_select_topk)",
                        "compact": "compact_kernel (bkv_compact)",
                        "update_beacons": "fps_kernel (bkv_update_beacons)"}[dom],
