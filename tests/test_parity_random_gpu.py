@@ -12,7 +12,7 @@ from parity import all_units, check_units, log, run_gpu
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 16
+N_CASES = 64
 
 
 def _workload(seed: int):
