@@ -165,7 +165,7 @@ def test_static_full_serving_shape_against_the_oracle():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(32))
 def test_static_random_geometries_bit_identical(seed):
     """Random small geometries (those of the random parity cases, without the beacon
     update): the default grouping fits the scratch, so every output is bit-identical to
