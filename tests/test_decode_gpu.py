@@ -105,3 +105,32 @@ def test_decode_chunk_sizes(n_layers, B, Hkv, cap, lens):
     bkv.decode_attention(shape, q, k, v, out, ws)
     torch.cuda.synchronize()
     log(f"[decode] chunks {n_layers}x{B}x{Hkv}: worst abs error {_check(shape, q, k, v, out):.2e}")
+
+
+def _random_geometry(seed):
+    """Seeded geometry: head_dim 64/128, groups 1-8, 1-4 KV heads, one to three sequences,
+    capacities around the 1024-key chunk (and tiny), lengths 0, 1, full or random."""
+    import random
+    rng = random.Random(seed)
+    D = rng.choice([64, 128])
+    hkv = rng.choice([1, 2, 4])
+    g = rng.randint(1, 8)
+    B = rng.choice([1, 2, 3])
+    cap = rng.choice([1, 31, 64, 300, 1023, 1024, 1025, 2049, 4100])
+    lens = tuple(rng.choice([0, 1, cap, rng.randint(0, cap)]) for _ in range(B))
+    return B, hkv * g, hkv, D, cap, lens, rng.choice([0.5, 1.0, 2.0, 3.0]), rng.choice([1, 2])
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_decode_random_geometries(seed):
+    B, Hq, Hkv, D, cap, lens, scale, nl = _random_geometry(3000 + seed)
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    seq = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    shape = bkv.CacheShape(nl, B, Hq, Hkv, D, cap, seq)
+    q, k, v = _random(shape, gen, scale)
+    out = [torch.empty((B, Hq, D), dtype=torch.float32, device="cuda") for _ in range(nl)]
+    ws = bkv.alloc_workspace(bkv.decode_workspace_bytes(shape))
+    bkv.decode_attention(shape, q, k, v, out, ws)
+    torch.cuda.synchronize()
+    log(f"[decode] seed {seed}: B{B} Hq/Hkv {Hq}/{Hkv} D{D} cap {cap} lens {lens}: "
+        f"worst abs error {_check(shape, q, k, v, out):.2e}")
