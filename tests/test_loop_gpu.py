@@ -84,3 +84,34 @@ def test_loop_beacons_filling_up_and_head_dim_64():
 def test_loop_recent_only_and_mean():
     _run(LoopConfig(n_layers=1, batch=2, n_q_heads=8, n_kv_heads=4, head_dim=128, budget=256, window=32, nb_max=0,
                     interval=128, aggregation="mean"), cycles=2)
+
+
+def _random_config(seed):
+    """Seeded loop configuration: head_dim 64/128, groups 1-8, 1-4 KV heads, budgets of 1
+    to 400 rows, intervals of 1 to 200 tokens, windows up to 32 (within both), 0-16
+    beacon slots with a random number live, max or mean aggregation."""
+    import random
+    rng = random.Random(seed)
+    D = rng.choice([64, 128])
+    hkv = rng.choice([1, 2, 4])
+    g = rng.randint(1, 8)
+    budget = rng.randint(1, 400)
+    interval = rng.randint(1, 200)
+    window = rng.randint(0, min(budget, interval, 32))
+    nb_max = rng.choice([0, 1, 4, 8, 16])
+    while g * window + nb_max > 512:
+        window //= 2
+    if g * window + nb_max == 0:
+        window = 1
+    n_live = rng.randint(0, nb_max)
+    cfg = LoopConfig(n_layers=rng.choice([1, 2]), batch=rng.choice([1, 2, 3]), n_q_heads=hkv * g, n_kv_heads=hkv,
+                     head_dim=D, budget=budget, window=window, nb_max=nb_max, interval=interval,
+                     aggregation=rng.choice(["max", "max", "mean"]))
+    return cfg, n_live
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_loop_random_configurations(seed):
+    cfg, n_live = _random_config(7000 + seed)
+    log(f"[loop] seed {seed}: {cfg} live beacons {n_live}")
+    _run(cfg, cycles=2, n_live=n_live)
