@@ -154,13 +154,13 @@ struct FpsArgs {
 constexpr int kDecodeMaxGroup = 8;     // query heads per KV head
 
 // Keys per decode workgroup (4 waves, each a quarter in blocks of 64 keys): 1024, or 512 or
-// 256 when larger chunks would leave fewer than kDecodeMinGrid workgroups per launch (about
-// 1.25 per CU of MI355X).  Measured: a 64-unit launch over 2048 keys took 34 us with 1024-key
-// chunks and 25 us with 256; a 112-unit launch over 4096 keys (448 workgroups) was 4% faster
-// with 1024 than with 256.
+// 256 when larger chunks would leave fewer than kDecodeMinGrid workgroups per launch (four
+// per CU of MI355X).  Measured: a 64-unit launch over 2048 keys took 34 us with 1024-key
+// chunks and 25 us with 256; a 112-unit launch over 4096 keys (448 workgroups of 1024 keys)
+// took 62.5 us with 1024-key chunks, 68 us with 512 and 59 us with 256.
 constexpr int kDecodeMaxChunk = 1024;
 constexpr int kDecodeMinChunk = 256;
-constexpr int kDecodeMinGrid = 320;
+constexpr int kDecodeMinGrid = 1024;
 inline int decode_chunk_keys(long long launch_units, int capacity) {
   int c = kDecodeMaxChunk;
   while (c > kDecodeMinChunk && launch_units * ((capacity + c - 1) / c) < kDecodeMinGrid)

@@ -90,8 +90,9 @@ def test_decode_every_group_size(G, D):
 
 
 @pytest.mark.parametrize("n_layers,B,Hkv,cap,lens", [
-    (4, 10, 8, 1100, (1100, 1025, 3, 0, 700, 1024, 1099, 64, 65, 512)),   # 640 workgroups of 1024 keys
-    (3, 5, 8, 1500, (1500, 1, 1025, 513, 257)),                           # 120 units: 512-key chunks
+    (4, 16, 8, 1100, (1100, 1025, 3, 0, 700, 1024, 1099, 64, 65, 512, 1100, 2, 1023, 300, 0, 1100)),
+    # ^ 512 units, 1024 workgroups of 1024 keys
+    (4, 10, 8, 2000, (2000, 1, 1025, 513, 257, 0, 1999, 64, 1024, 1536)),       # 320 units: 512-key chunks
 ])
 def test_decode_chunk_sizes(n_layers, B, Hkv, cap, lens):
     """The chunk size follows the launch size (1024 keys per workgroup for large launches,
